@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Benchmark of the BF16 skinny GEMM on one MI355X.
+
+One step = one hipGraph replay that runs every (shape, M) cell of the workload,
+each over rotated copies of its weight adding up to at least 1 GiB, so that
+every call streams its weight from HBM rather than from the 256 MB Infinity
+Cache (the cold-cache protocol of the vLLM SM90 plan page, section "How it was
+measured": chains over copies of the weight totalling 1 GiB or more, captured
+in a graph). Inputs are synthetic and seeded (x ~ N(0,1), W ~ N(0,1/K)).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+    python bench.py [--steps K] [--warmup W] [--workload kda|single|mla|lm_head|chain]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "cold-cache µs/call and achieved HBM GB/s (% of peak) at M=1/2/4 per (N,K)"
+PEAK_HBM_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+ROTATE_BYTES = 1 << 30  # >= 1 GiB of weight copies per cell (4x the 256 MB Infinity Cache)
+
+# (name, [(N, K, M), ...]) -- the shapes of the decode projections
+WORKLOADS = {
+    "kda": ("KDA in_proj (12576,4096) + o_proj (4096,4096) at M=1,2,4, cold cache",
+            [(12576, 4096, m) for m in (1, 2, 4)] + [(4096, 4096, m) for m in (1, 2, 4)]),
+    "single": ("single skinny GEMM (4096,1024) at M=1, cold cache", [(4096, 1024, 1)]),
+    "mla": ("MLA/shared-expert (2048,4096) (4096,1024) (8192,1536) (4096,8192) at M=1,2,4 "
+            "+ paired 2x(4096,128), cold cache",
+            [(n, k, m) for (n, k) in ((2048, 4096), (4096, 1024), (8192, 1536), (4096, 8192))
+             for m in (1, 2, 4)] + [("pair", 4096, 128, m) for m in (1, 2, 4)]),
+    "lm_head": ("LM head (77440,4096) at M=1,2,4, cold cache", [(77440, 4096, m) for m in (1, 2, 4)]),
+}
+CHAIN = [(12576, 4096, 34), (4096, 4096, 34), (2048, 4096, 53), (4096, 1024, 42),
+         (8192, 1536, 11), (4096, 8192, 11), (77440, 4096, 1)]
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="kda", choices=sorted(list(WORKLOADS) + ["chain"]))
+    ap.add_argument("--chain-m", type=int, default=1, help="M of the decode-chain workload")
+    ap.add_argument("--trials", type=int, default=5, help="per-cell timing trials")
+    ap.add_argument("--replays", type=int, default=20, help="graph replays per per-cell trial")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample budget")
+    ap.add_argument("--no-parity", action="store_true")
+    return ap.parse_args()
+
+
+def bytes_per_call(cell) -> int:
+    if cell[0] == "pair":
+        _, N, K, M = cell
+        return 4 * N * K + 2 * M * K + 4 * M * N
+    N, K, M = cell
+    return 2 * N * K + 2 * M * K + 2 * M * N
+
+
+def cell_name(cell) -> str:
+    if cell[0] == "pair":
+        return f"pair2x({cell[1]},{cell[2]})M{cell[3]}"
+    return f"({cell[0]},{cell[1]})M{cell[2]}"
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the GEMV shards by output rows with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bf16_skinny_gemm_amd as skg
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    skg.skinny_gemm_init(0)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def to_host(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    # ---------------- inputs ----------------
+    calls = []      # (cell, fn) in step order
+    cells = []      # per cell: dict with buffers
+    if args.workload == "chain":
+        M = args.chain_m
+        desc = f"decode-step projection chain, 186 distinct weights, M={M}"
+        gen = torch.Generator(device=dev)
+        xs = {}
+        tid = 0
+        for (N, K, count) in CHAIN:
+            if K not in xs:
+                xs[K] = to_dev(synth.activations(M, K, seed=0, shape_id=K, tensor_id=0))
+            ws = []
+            for _ in range(count):
+                gen.manual_seed(1000 + tid)
+                tid += 1
+                w = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+                w.copy_(torch.randn((N, K), generator=gen, device=dev) * (1.0 / math.sqrt(K)))
+                ws.append(w)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            cells.append({"cell": (N, K, M), "x": xs[K], "ws": ws, "y": y, "calls": count})
+        log(f"chain weights resident: {sum(c['ws'][0].numel() * 2 * len(c['ws']) for c in cells) / 1e9:.2f} GB")
+    else:
+        desc, cell_list = WORKLOADS[args.workload]
+        for i, cell in enumerate(cell_list):
+            if cell[0] == "pair":
+                _, N, K, M = cell
+                w0 = synth.weights(N, K, seed=0, shape_id=N * 7 + K, tensor_id=1)
+                w1 = synth.weights(N, K, seed=0, shape_id=N * 7 + K, tensor_id=2)
+                copies = max(1, math.ceil(ROTATE_BYTES / (4 * N * K)))
+                W0d, W1d = to_dev(w0), to_dev(w1)
+                ws = [(W0d, W1d)] + [(W0d.clone(), W1d.clone()) for _ in range(copies - 1)]
+                host_w = (w0, w1)
+                y = (torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                     torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            else:
+                N, K, M = cell
+                wb = synth.weights(N, K, seed=0, shape_id=N * 7 + K, tensor_id=1)
+                copies = max(1, math.ceil(ROTATE_BYTES / (2 * N * K)))
+                Wd = to_dev(wb)
+                ws = [Wd] + [Wd.clone() for _ in range(copies - 1)]
+                host_w = wb
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            xb = synth.activations(M, K, seed=0, shape_id=N * 7 + K, tensor_id=0)
+            cells.append({"cell": cell, "x": to_dev(xb), "xb": xb, "ws": ws, "y": y,
+                          "calls": len(ws), "host_w": host_w})
+            log(f"cell {cell_name(cell)}: {len(ws)} weight copies")
+    torch.cuda.synchronize()
+
+    def run_cell(c):
+        cell = c["cell"]
+        if cell[0] == "pair":
+            for (w0, w1) in c["ws"]:
+                skg.gemm_pair(c["x"], w0, w1, out0=c["y"][0], out1=c["y"][1])
+        else:
+            for w in c["ws"]:
+                skg.gemm(c["x"], w, out=c["y"])
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()  # eager warm-up on the capture stream
+            with torch.cuda.graph(g, stream=s):
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        return g
+
+    def step_fn():
+        for c in cells:
+            run_cell(c)
+
+    step_bytes = sum(bytes_per_call(c["cell"]) * c["calls"] for c in cells)
+    step_calls = sum(c["calls"] for c in cells)
+    log(f"capturing step: {step_calls} launches, {step_bytes / 1e9:.3f} GB per step")
+    g_step = capture(step_fn)
+
+    # ---------------- timed steps ----------------
+    for _ in range(args.warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        g_step.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(end) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step: {ms_per_step:.4f} ms, {value:.1f} GB/s (wall {wall:.3f} s for {args.steps} steps)")
+
+    # ---------------- per-cell timing (events on the launch stream) ----------------
+    cell_rows = []
+    for c in cells:
+        g = capture(lambda c=c: run_cell(c))
+        g.replay()
+        torch.cuda.synchronize()
+        per_call = []
+        for _ in range(args.trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.replays):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per_call.append(e0.elapsed_time(e1) * 1e3 / (args.replays * c["calls"]))
+        us = statistics.median(per_call)
+        b = bytes_per_call(c["cell"])
+        gbps = b / (us * 1e-6) / 1e9
+        row = {"cell": cell_name(c["cell"]), "us_per_call": round(us, 3),
+               "us_min": round(min(per_call), 3), "us_max": round(max(per_call), 3),
+               "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+               "bytes_per_call": b, "calls_per_replay": c["calls"]}
+        if c["cell"][0] != "pair":
+            N, K, M = c["cell"]
+            p, tuned = skg.skinny_gemm_get_plan(N, K, M)
+            row["plan"] = p.as_dict()
+            row["tuned_plan"] = tuned
+        cell_rows.append(row)
+        log(f"cell {row['cell']}: {us:.3f} us/call, {gbps:.1f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
+        del g
+
+    # the dominant kernel: the cell moving the most bytes per launch (first such cell)
+    dom = max(cell_rows, key=lambda r: (r["bytes_per_call"], -cell_rows.index(r)))
+    roofline = {"bound": "hbm", "kernel": dom["cell"], "achieved": dom["gbps"],
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(dom["gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
+                "avg_launch_us": dom["us_per_call"], "algorithmic_bytes_per_launch": dom["bytes_per_call"]}
+
+    # ---------------- parity spot check of the timed buffers ----------------
+    parity = None
+    if not args.no_parity and args.workload != "chain":
+        import oracle
+
+        ok = True
+        worst = 0.0
+        for c in cells:
+            cell = c["cell"]
+            g = np.random.default_rng(0)
+            if cell[0] == "pair":
+                N = cell[1]
+                rows = np.unique(g.integers(0, N, 256)).astype(np.int64)
+                for yt, wb in zip(c["y"], c["host_w"]):
+                    yr, ref, mag = oracle.gemm_rows(c["xb"], wb, rows)
+                    r = oracle.acceptance(to_host(yt)[:, rows], yr, ref, mag, check_cosine=False)
+                    ok &= r["pass"]
+                    worst = max(worst, r["max_s1_ratio"])
+            else:
+                N = cell[0]
+                rows = np.unique(np.concatenate([np.arange(min(N, 64)), np.arange(N - 64, N),
+                                                 g.integers(0, N, 256)])).astype(np.int64)
+                yr, ref, mag = oracle.gemm_rows(c["xb"], c["host_w"], rows)
+                r = oracle.acceptance(to_host(c["y"])[:, rows], yr, ref, mag, check_cosine=False)
+                ok &= r["pass"]
+                worst = max(worst, r["max_s1_ratio"])
+        parity = {"pass": bool(ok), "max_s1_ratio": round(worst, 4), "sampled": True}
+        log(f"parity spot check: {parity}")
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu and args.workload != "chain":
+        import oracle
+
+        nt = oracle.default_threads()
+        done_bytes = 0
+        t_cpu = 0.0
+        passes = 0
+        while t_cpu < args.cpu_seconds and passes < 50:
+            for c in cells:
+                cell = c["cell"]
+                t1 = time.perf_counter()
+                if cell[0] == "pair":
+                    oracle.gemm_pair(c["xb"], c["host_w"][0], c["host_w"][1], nthreads=nt)
+                else:
+                    oracle.gemm(c["xb"], c["host_w"], nthreads=nt)
+                t_cpu += time.perf_counter() - t1
+                done_bytes += bytes_per_call(cell)
+            passes += 1
+        cpu = {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": nt,
+               "kind": "oracle",
+               "sample": f"{passes} pass(es) of one call per cell of the workload "
+                         f"({len(cells)} cells), fp64 C oracle, {t_cpu:.1f} s"}
+        log(f"cpu oracle: {cpu}")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": desc, "launches_per_step": step_calls,
+                   "bytes_per_step": step_bytes, "rotation_bytes_min": ROTATE_BYTES,
+                   "accumulate": "fp32", "device": props.name},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "cells": cell_rows,
+        "parity": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

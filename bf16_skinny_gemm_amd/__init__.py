@@ -1,0 +1,261 @@
+"""BF16 skinny GEMM for MI355X (gfx950): y[M,N] = x[M,K] . W[N,K]^T for M = 1..4.
+
+Thin Python binding over the C ABI of ``libskinny_gemm_bf16.so``
+(``include/skinny_gemm.h``). Every step of the computation runs in the HIP
+kernels; this module only marshals arguments. PyTorch provides device memory
+and the current stream. There is no fallback: if the library is missing, or the
+device is not gfx950, calls raise.
+
+Raw entry points (same names and arguments as the C functions; pointers as
+Python ints; a non-zero status raises :class:`SkinnyError`):
+    skinny_gemm_init, skinny_gemm_bf16, skinny_gemm_bf16_pair,
+    skinny_gemm_bf16_ex, skinny_gemm_bf16_pair_ex, skinny_gemm_get_plan,
+    skinny_gemm_num_variants, skinny_gemm_get_variant,
+    skinny_gemm_status_string, skinny_gemm_version
+
+Tensor helpers: :func:`gemm` and :func:`gemm_pair`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+# torch first: its HIP runtime (soname libamdhip64.so.7) must be the one the
+# library binds to, so that torch's stream handles are valid in it.
+import torch
+
+from .build import LIB_PATH
+
+SKINNY_OK = 0
+SKINNY_ERR_INVALID_ARG = -1
+SKINNY_ERR_UNSUPPORTED = -2
+SKINNY_ERR_NOT_INITIALIZED = -3
+SKINNY_ERR_LAUNCH = -4
+
+SKINNY_KIND_FIXED_K = 1
+SKINNY_KIND_LOOP_K = 2
+SKINNY_KIND_SCALAR = 3
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status)} (status {status})")
+
+
+class Plan(ctypes.Structure):
+    """skinny_plan_t."""
+
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("threads_per_block", ctypes.c_int32),
+        ("lanes_per_row", ctypes.c_int32),
+        ("chunks", ctypes.c_int32),
+        ("rows_per_wave", ctypes.c_int32),
+        ("k_split", ctypes.c_int32),
+        ("nontemporal", ctypes.c_int32),
+        ("grid_blocks", ctypes.c_int32),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d: dict) -> "Plan":
+        return cls(**{f: int(d[f]) for f, _ in cls._fields_})
+
+    def __repr__(self) -> str:
+        return "Plan(" + ", ".join(f"{k}={v}" for k, v in self.as_dict().items()) + ")"
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it first (python -m bf16_skinny_gemm_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        i = ctypes.c_int
+        pp = ctypes.POINTER(Plan)
+        L.skinny_gemm_init.argtypes = [i]
+        L.skinny_gemm_bf16.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.skinny_gemm_bf16_pair.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp]
+        L.skinny_gemm_bf16_ex.argtypes = [vp, vp, vp, i, i, i, pp, vp]
+        L.skinny_gemm_bf16_pair_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, pp, vp]
+        L.skinny_gemm_get_plan.argtypes = [i, i, i, pp]
+        L.skinny_gemm_num_variants.argtypes = []
+        L.skinny_gemm_get_variant.argtypes = [i, pp]
+        L.skinny_gemm_status_string.argtypes = [i]
+        L.skinny_gemm_status_string.restype = ctypes.c_char_p
+        L.skinny_gemm_version.argtypes = []
+        for name in ("skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair",
+                     "skinny_gemm_bf16_ex", "skinny_gemm_bf16_pair_ex", "skinny_gemm_get_plan",
+                     "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def _status_string(status: int) -> str:
+    try:
+        return lib().skinny_gemm_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - library not loadable
+        return "unknown status"
+
+
+def _check(status: int, where: str) -> int:
+    if status < 0:
+        raise SkinnyError(status, where)
+    return status
+
+
+# ---- raw entry points (same names as the C ABI) -----------------------------
+
+def skinny_gemm_init(device: int) -> None:
+    _check(lib().skinny_gemm_init(int(device)), "skinny_gemm_init")
+
+
+def skinny_gemm_bf16(x: int, W: int, y: int, M: int, N: int, K: int, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16(x, W, y, M, N, K, stream), "skinny_gemm_bf16")
+
+
+def skinny_gemm_bf16_pair(x: int, W0: int, W1: int, y0: int, y1: int, M: int, N: int, K: int,
+                          stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_pair(x, W0, W1, y0, y1, M, N, K, stream), "skinny_gemm_bf16_pair")
+
+
+def skinny_gemm_bf16_ex(x: int, W: int, y: int, M: int, N: int, K: int, plan: Plan,
+                        stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_ex(x, W, y, M, N, K, ctypes.byref(plan), stream),
+           "skinny_gemm_bf16_ex")
+
+
+def skinny_gemm_bf16_pair_ex(x: int, W0: int, W1: int, y0: int, y1: int, M: int, N: int, K: int,
+                             plan: Plan, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_pair_ex(x, W0, W1, y0, y1, M, N, K, ctypes.byref(plan), stream),
+           "skinny_gemm_bf16_pair_ex")
+
+
+def skinny_gemm_get_plan(N: int, K: int, M: int) -> tuple[Plan, bool]:
+    """(plan, tuned): the plan skinny_gemm_bf16 uses for (N, K, M)."""
+    p = Plan()
+    r = _check(lib().skinny_gemm_get_plan(N, K, M, ctypes.byref(p)), "skinny_gemm_get_plan")
+    return p, bool(r == 1)
+
+
+def skinny_gemm_num_variants() -> int:
+    return lib().skinny_gemm_num_variants()
+
+
+def skinny_gemm_get_variant(index: int) -> Plan:
+    p = Plan()
+    _check(lib().skinny_gemm_get_variant(index, ctypes.byref(p)), "skinny_gemm_get_variant")
+    return p
+
+
+def skinny_gemm_status_string(status: int) -> str:
+    return _status_string(status)
+
+
+def skinny_gemm_version() -> int:
+    return lib().skinny_gemm_version()
+
+
+def variants() -> list[Plan]:
+    return [skinny_gemm_get_variant(i) for i in range(skinny_gemm_num_variants())]
+
+
+# ---- tensor helpers ---------------------------------------------------------
+
+def _stream_handle(device: torch.device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(t: torch.Tensor, name: str, ndim: int = 2) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemm(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
+         plan: Plan | None = None) -> torch.Tensor:
+    """y = x @ W.T for bfloat16 x [M, K] (M <= 4) and W [N, K]; one kernel launch
+    on the current stream."""
+    _check_tensor(x, "x")
+    _check_tensor(W, "W")
+    M, K = x.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: x {tuple(x.shape)}, W {tuple(W.shape)}")
+    if W.device != x.device:
+        raise ValueError("x and W must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (M, N) or out.device != x.device:
+            raise ValueError(f"out must be [{M}, {N}] on {x.device}")
+    s = _stream_handle(x.device)
+    with torch.cuda.device(x.device):
+        if plan is None:
+            skinny_gemm_bf16(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, s)
+        else:
+            skinny_gemm_bf16_ex(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, plan, s)
+    return out
+
+
+def gemm_pair(x: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
+              out0: torch.Tensor | None = None, out1: torch.Tensor | None = None,
+              plan: Plan | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(x @ W0.T, x @ W1.T) for two same-shape bfloat16 weights, one kernel launch."""
+    _check_tensor(x, "x")
+    _check_tensor(W0, "W0")
+    _check_tensor(W1, "W1")
+    M, K = x.shape
+    if tuple(W0.shape) != tuple(W1.shape) or W0.shape[1] != K:
+        raise ValueError(f"shapes: x {tuple(x.shape)}, W0 {tuple(W0.shape)}, W1 {tuple(W1.shape)}")
+    N = W0.shape[0]
+    outs = []
+    for o, name in ((out0, "out0"), (out1, "out1")):
+        if o is None:
+            o = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        else:
+            _check_tensor(o, name)
+            if tuple(o.shape) != (M, N):
+                raise ValueError(f"{name} must be [{M}, {N}]")
+        outs.append(o)
+    s = _stream_handle(x.device)
+    with torch.cuda.device(x.device):
+        if plan is None:
+            skinny_gemm_bf16_pair(x.data_ptr(), W0.data_ptr(), W1.data_ptr(), outs[0].data_ptr(),
+                                  outs[1].data_ptr(), M, N, K, s)
+        else:
+            skinny_gemm_bf16_pair_ex(x.data_ptr(), W0.data_ptr(), W1.data_ptr(), outs[0].data_ptr(),
+                                     outs[1].data_ptr(), M, N, K, plan, s)
+    return outs[0], outs[1]
+
+
+__all__ = [
+    "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair",
+    "skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",
+    "skinny_gemm_bf16_pair_ex", "skinny_gemm_get_plan", "skinny_gemm_num_variants",
+    "skinny_gemm_get_variant", "skinny_gemm_status_string", "skinny_gemm_version",
+    "SKINNY_OK", "SKINNY_ERR_INVALID_ARG", "SKINNY_ERR_UNSUPPORTED", "SKINNY_ERR_NOT_INITIALIZED",
+    "SKINNY_ERR_LAUNCH", "SKINNY_KIND_FIXED_K", "SKINNY_KIND_LOOP_K", "SKINNY_KIND_SCALAR",
+]

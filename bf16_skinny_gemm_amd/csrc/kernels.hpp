@@ -1,0 +1,391 @@
+// Device code of the BF16 skinny GEMM for gfx950 (CDNA4, wave64).
+//
+// y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),  M <= 4 rows of x, W [N][K] row-major.
+//
+// At M <= 4 the product does M flops per weight byte, so its speed is the speed
+// at which W streams out of HBM (the pages' "% of HBM peak = weight bytes /
+// time / peak", vLLM SM90 plan page, section Validation). Everything below is
+// arranged around keeping enough 128-bit weight loads in flight on every CU:
+//
+//  * a wavefront reads W with raw buffer loads of 16 bytes per lane; the
+//    64 lanes are split into groups of LPR lanes, each group covering one row,
+//    so one load instruction touches 64/LPR rows with LPR*16 contiguous bytes
+//    each. A buffer resource whose size ends at the last valid row turns the
+//    loads of rows >= N into zeros, so the N tail needs no branches;
+//  * x (at most 4 rows) stays on chip: in registers for the compile-time-K
+//    family (each lane keeps only the K positions it multiplies), in LDS for
+//    the looped-K family;
+//  * products are accumulated in float32 with v_dot2c_f32_bf16 (two bf16
+//    products added into a float32 accumulator per instruction);
+//  * partial sums of a row meet across its LPR lanes by DPP lane permutations
+//    and row broadcasts, then across the k_split waves of a block in LDS,
+//    always in one fixed order (deterministic results);
+//  * the float32 sum is rounded once to bfloat16, nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skg {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Third dword of a gfx9-family buffer resource: 32-bit raw data format, no
+// swizzle, so buffer_load_dwordx4 reads 16 plain bytes and reads outside
+// [0, num_records) return zero.
+constexpr int kBufferFlags = 0x00020000;
+// Cache-policy bits of a gfx94x/gfx950 buffer instruction: bit 1 = nt.
+constexpr int kAuxNontemporal = 2;
+// A byte offset that is always outside the resource: its load returns zeros.
+constexpr unsigned kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufferFlags);
+}
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned byte_offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_offset, 0, NT ? kAuxNontemporal : 0);
+}
+
+// acc + w.lo*x.lo + w.hi*x.hi, the two bfloat16 products exact, float32 sum.
+__device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                           __builtin_bit_cast(bf16x2_t, x), acc, false);
+}
+
+__device__ __forceinline__ float dot8(const u32x4 &w, const u32x4 &x, float acc)
+{
+    acc = dot2(w[0], x[0], acc);
+    acc = dot2(w[1], x[1], acc);
+    acc = dot2(w[2], x[2], acc);
+    acc = dot2(w[3], x[3], acc);
+    return acc;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h)
+{
+    return __builtin_bit_cast(float, (unsigned)h << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, f);
+    const unsigned r = u + 0x7FFFu + ((u >> 16) & 1u);
+    uint16_t out = (uint16_t)(r >> 16);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
+        out = (uint16_t)((u >> 16) | 0x0040u);
+    return out;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    // Rows outside ROW_MASK take `old` = 0 and so keep v.
+    const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false);
+    return v + __builtin_bit_cast(float, moved);
+}
+
+// Lane of an LPR-lane group that holds the group's sum after group_sum<LPR>.
+template <int LPR>
+constexpr int sum_lane() { return LPR >= 32 ? LPR - 1 : 0; }
+
+// Sum over groups of LPR consecutive lanes (LPR = 1, 2, 4, ..., 64). For
+// LPR <= 16 every lane of a group ends with the group's sum; for 32 and 64 the
+// last lane of the group does (sum_lane). Must run with all 64 lanes active.
+// The cross-row steps use the DPP row broadcasts, not the gfx950 permlane
+// swaps: clang folds the two results of permlane{16,32}_swap(v, v) into one,
+// which silently breaks a butterfly built on them.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v)
+{
+    if constexpr (LPR >= 2)
+        v = dpp_add<0xB1>(v);        // quad_perm [1,0,3,2]: lane ^ 1
+    if constexpr (LPR >= 4)
+        v = dpp_add<0x4E>(v);        // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8)
+        v = dpp_add<0x141>(v);       // row_half_mirror: the other quad of each 8 lanes
+    if constexpr (LPR >= 16)
+        v = dpp_add<0x140>(v);       // row_mirror: the other half of each 16-lane row
+    if constexpr (LPR >= 32)
+        v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3: lanes 31, 63 hold 32-sums
+    if constexpr (LPR >= 64)
+        v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3: lane 63 holds the 64-sum
+    return v;
+}
+
+struct Args {
+    const uint16_t *x;
+    const uint16_t *w0;
+    const uint16_t *w1;  // second weight of the pair (== w0 when nmats == 1)
+    uint16_t *y0;
+    uint16_t *y1;
+    int N;
+    int K;
+    int tiles_per_mat;   // ceil(N / rows per tile)
+    int total_tiles;     // nmats * tiles_per_mat
+};
+
+// ---------------------------------------------------------------------------
+// Family FIXED_K: K = KW * LPR * 8 * CH known at compile time, x in registers.
+//
+// A block has W waves (a launch-time value, W % KW == 0) in W/KW groups; the
+// KW waves of a group share the same rows and split K into KW slices. A tile
+// is the rows the block covers per iteration, (W/KW) * ROWS_W consecutive
+// rows; each group owns ROWS_W = R * 64/LPR of them.
+// Lane (sub, kl) = (lane / LPR, lane % LPR) reads, for row r*RPI + sub of its
+// group and chunk j < CH, the 8 elements starting at
+//     kw * K/KW + j * LPR*8 + kl * 8.
+// ---------------------------------------------------------------------------
+constexpr int kMaxWaves = 8;  // largest block: 512 threads
+
+template <int M, int LPR, int CH, int R, int KW, bool NT>
+__global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
+{
+    constexpr int K = KW * LPR * 8 * CH;
+    constexpr int KSLICE = K / KW;
+    constexpr int RPI = 64 / LPR;
+    constexpr int ROWS_W = R * RPI;
+    static_assert(64 % LPR == 0 && LPR >= 8, "lanes per row: 8, 16, 32 or 64");
+    static_assert(kMaxWaves % KW == 0, "k_split must divide the largest block");
+
+    // The host launches blockDim.x = 64 * waves with waves % KW == 0.
+    const int groups = (int)(blockDim.x >> 6) / KW;
+    const int rows_t = groups * ROWS_W;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kw = wave % KW;
+    const int grp = wave / KW;
+    const int sub = lane / LPR;
+    const int kl = lane % LPR;
+    const unsigned kbase = (unsigned)(kw * KSLICE + kl * 8);
+
+    // This lane's K positions of every x row.
+    u32x4 xr[M][CH];
+    {
+        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
+    }
+
+    __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
+
+    for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+        const int mat = tile >= a.tiles_per_mat ? 1 : 0;
+        const int t = tile - mat * a.tiles_per_mat;
+        const uint16_t *wm = mat ? a.w1 : a.w0;
+        uint16_t *ym = mat ? a.y1 : a.y0;
+        const int row0 = t * rows_t + grp * ROWS_W;
+        int valid = a.N - row0;
+        valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
+        const __amdgpu_buffer_rsrc_t ws =
+            make_rsrc(wm + (size_t)row0 * K, (unsigned)(valid * K * 2));
+
+        u32x4 wv[R][CH];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                wv[r][j] = load16<NT>(ws, ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u);
+
+        float acc[M][R];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float s = 0.0f;
+#pragma unroll
+                for (int j = 0; j < CH; ++j)
+                    s = dot8(wv[r][j], xr[m][j], s);
+                acc[m][r] = group_sum<LPR>(s);
+            }
+
+        constexpr int OUT = sum_lane<LPR>();
+        if constexpr (KW == 1) {
+            if (kl == OUT) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = row0 + r * RPI + sub;
+                    if (row < a.N) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+                            ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m][r]);
+                    }
+                }
+            }
+        } else {
+            if (kl == OUT) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        part[((grp * KW + kw) * M + m) * ROWS_W + r * RPI + sub] = acc[m][r];
+            }
+            __syncthreads();
+            if (kw == 0 && kl == OUT) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = row0 + r * RPI + sub;
+                    if (row < a.N) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            float s = part[((grp * KW + 0) * M + m) * ROWS_W + r * RPI + sub];
+#pragma unroll
+                            for (int q = 1; q < KW; ++q)
+                                s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
+                            ym[(size_t)m * a.N + row] = f32_to_bf16(s);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Family LOOP_K: any K with K % 8 == 0. One wave = one group of R rows (64
+// lanes per row); x is staged once per block into LDS as [M][Kpad] with a zero
+// tail up to a multiple of 512*U, and the K loop keeps U loads per row in
+// flight. Weight chunks past K use an out-of-range offset and read as zeros.
+// ---------------------------------------------------------------------------
+template <int M, int U, int R, bool NT>
+__global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad)
+{
+    extern __shared__ u32x4 lds_x[];  // [M][kpad / 8]
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int K = a.K;
+    const int kvec = kpad / 8;
+
+    {
+        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+        for (int i = threadIdx.x; i < M * kvec; i += (int)blockDim.x) {
+            const int m = i / kvec;
+            const int kv = i - m * kvec;
+            const unsigned off = kv * 8 < K ? (unsigned)(m * K + kv * 8) * 2u : kOutOfRange;
+            lds_x[i] = load16<false>(xs, off);
+        }
+        __syncthreads();
+    }
+
+    const int rows_t = (int)(blockDim.x >> 6) * R;
+    for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
+        const int mat = tile >= a.tiles_per_mat ? 1 : 0;
+        const int t = tile - mat * a.tiles_per_mat;
+        const uint16_t *wm = mat ? a.w1 : a.w0;
+        uint16_t *ym = mat ? a.y1 : a.y0;
+        const int row0 = t * rows_t + wave * R;
+        int valid = a.N - row0;
+        valid = valid < 0 ? 0 : (valid > R ? R : valid);
+        const __amdgpu_buffer_rsrc_t ws =
+            make_rsrc(wm + (size_t)row0 * K, (unsigned)(valid * K * 2));
+
+        float acc[M][R];
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = 0.0f;
+
+        for (int k0 = 0; k0 < K; k0 += 512 * U) {
+            u32x4 wv[R][U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + u * 512 + lane * 8;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    wv[r][u] = load16<NT>(ws, k < K ? (unsigned)(r * K + k) * 2u : kOutOfRange);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int kv = (k0 + u * 512) / 8 + lane;
+#pragma unroll
+                for (int m = 0; m < M; ++m) {
+                    const u32x4 xv = lds_x[m * kvec + kv];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[m][r] = dot8(wv[r][u], xv, acc[m][r]);
+                }
+            }
+        }
+
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = group_sum<64>(acc[m][r]);
+
+        if (lane == sum_lane<64>()) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = row0 + r;
+                if (row < a.N) {
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m][r]);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Family SCALAR: any K, any alignment. One wave per output row (pair rows
+// follow the first weight's rows), lanes stride K one element at a time,
+// float32 fused multiply-add on exactly widened bfloat16 values.
+// ---------------------------------------------------------------------------
+template <int M>
+__global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
+{
+    const int lane = threadIdx.x & 63;
+    const long long g = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= (long long)nmats * a.N)
+        return;  // whole wave
+    const int mat = g >= a.N ? 1 : 0;
+    const int row = (int)(g - (long long)mat * a.N);
+    const uint16_t *w = (mat ? a.w1 : a.w0) + (size_t)row * a.K;
+    uint16_t *ym = mat ? a.y1 : a.y0;
+
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        acc[m] = 0.0f;
+    for (int k = lane; k < a.K; k += 64) {
+        const float wf = bf16_to_f32(w[k]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            acc[m] = __builtin_fmaf(bf16_to_f32(a.x[(size_t)m * a.K + k]), wf, acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        acc[m] = group_sum<64>(acc[m]);
+    if (lane == sum_lane<64>()) {
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m]);
+    }
+}
+
+// K == 0: the empty sum, +0 everywhere.
+__global__ __launch_bounds__(256) void zero_kernel(uint16_t *y0, uint16_t *y1, long long count)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < count) {
+        y0[i] = 0;
+        if (y1)
+            y1[i] = 0;
+    }
+}
+
+}  // namespace skg

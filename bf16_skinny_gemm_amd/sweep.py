@@ -1,0 +1,228 @@
+"""On-device plan sweep for the skinny GEMM plan table.
+
+For each (N, K, M) it times every compiled variant that can run the shape,
+at several block sizes and with both grid modes (persistent, one block per
+tile), and keeps the fastest. This follows the pages' method (vLLM SM121 plan
+page, section Details: a graph-replay sweep over the plan knobs with the weight
+rotated out of the cache; SM90 plan page: a chain over weight copies of at
+least 1 GiB, captured in a graph, trials of replays), with the copies sized
+past the MI355X's 256 MB Infinity Cache.
+
+    python -m bf16_skinny_gemm_amd.sweep --out sweep.jsonl          # measure (GPU)
+    python -m bf16_skinny_gemm_amd.sweep --emit-inc sweep.jsonl      # write plans_gfx950.inc
+
+Measurements are appended one JSON line per (cell, plan); a rerun skips cells
+already complete in the output file, so an interrupted sweep resumes.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+INC_PATH = os.path.join(HERE, "csrc", "plans_gfx950.inc")
+ROTATE_BYTES = 1 << 30
+
+# The decode projections at M = 1, 2, 4 (and 3, which the API supports), plus the
+# paired (4096, 128) f_b/g_b weights, which are swept as pairs.
+SHAPES = [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536), (4096, 8192),
+          (77440, 4096)]
+PAIR_SHAPES = [(4096, 128)]
+MS = (1, 2, 3, 4)
+BIG_GRID = 1 << 30  # grid_blocks >= tile count: one block per tile
+
+
+def log(msg):
+    print(f"[sweep {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def candidate_plans(skg, K, M):
+    """Every (variant, block size, grid mode) able to run (K, M)."""
+    out = []
+    for v in skg.variants():
+        d = v.as_dict()
+        if d["kind"] == skg.SKINNY_KIND_SCALAR:
+            continue
+        if d["kind"] == skg.SKINNY_KIND_FIXED_K and \
+                d["k_split"] * d["lanes_per_row"] * 8 * d["chunks"] != K:
+            continue
+        for tpb in (128, 256, 512):
+            if (tpb // 64) % d["k_split"]:
+                continue
+            for grid in (0, BIG_GRID):
+                out.append(skg.Plan.from_dict({**d, "threads_per_block": tpb, "grid_blocks": grid}))
+    return out
+
+
+def plan_key(p) -> tuple:
+    d = p.as_dict()
+    return tuple(d[k] for k in ("kind", "threads_per_block", "lanes_per_row", "chunks",
+                                "rows_per_wave", "k_split", "nontemporal", "grid_blocks"))
+
+
+def time_plan(torch, skg, x, weights, ys, plan, pair, trials, replays):
+    """Median microseconds per call over graph replays of one call per weight copy."""
+    def run():
+        for w in weights:
+            if pair:
+                skg.gemm_pair(x, w[0], w[1], out0=ys[0], out1=ys[1], plan=plan)
+            else:
+                skg.gemm(x, w, out=ys, plan=plan)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / (replays * len(weights)))
+    del g
+    return statistics.median(per), min(per), max(per)
+
+
+def done_keys(path):
+    keys = set()
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                try:
+                    r = json.loads(line)
+                except json.JSONDecodeError:
+                    continue
+                if r.get("complete"):
+                    keys.add((r["N"], r["K"], r["M"], r["pair"]))
+    return keys
+
+
+def measure(args):
+    import torch
+
+    import bf16_skinny_gemm_amd as skg
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    skg.skinny_gemm_init(0)
+    done = done_keys(args.out)
+    cells = [(N, K, False) for (N, K) in SHAPES] + [(N, K, True) for (N, K) in PAIR_SHAPES]
+    if args.only:
+        want = {tuple(int(v) for v in s.split("x")) for s in args.only.split(",")}
+        cells = [c for c in cells if (c[0], c[1]) in want]
+    ms = tuple(int(m) for m in args.ms.split(","))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    with open(args.out, "a") as fout:
+        for (N, K, pair) in cells:
+            todo = [M for M in ms if (N, K, M, pair) not in done]
+            if not todo:
+                continue
+            wbytes = (4 if pair else 2) * N * K
+            copies = max(2, math.ceil(ROTATE_BYTES / wbytes))
+            base = (torch.randn((N, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+            if pair:
+                base1 = (torch.randn((N, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+                weights = [(base, base1)] + [(base.clone(), base1.clone()) for _ in range(copies - 1)]
+            else:
+                weights = [base] + [base.clone() for _ in range(copies - 1)]
+            log(f"shape ({N},{K}) pair={pair}: {copies} copies")
+            for M in todo:
+                x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+                ys = ((torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                       torch.empty((M, N), dtype=torch.bfloat16, device=dev)) if pair
+                      else torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+                nbytes = (4 * N * K + 2 * M * K + 4 * M * N) if pair else (2 * N * K + 2 * M * K + 2 * M * N)
+                best = None
+                for plan in candidate_plans(skg, K, M):
+                    try:
+                        us, lo, hi = time_plan(torch, skg, x, weights, ys, plan, pair,
+                                               args.trials, args.replays)
+                    except skg.SkinnyError:
+                        continue  # this M does not fit the variant
+                    rec = {"N": N, "K": K, "M": M, "pair": pair, "plan": plan.as_dict(),
+                           "us": round(us, 4), "us_min": round(lo, 4), "us_max": round(hi, 4),
+                           "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                    fout.write(json.dumps(rec) + "\n")
+                    if best is None or us < best[0]:
+                        best = (us, plan)
+                fout.write(json.dumps({"N": N, "K": K, "M": M, "pair": pair, "complete": True}) + "\n")
+                fout.flush()
+                log(f"  M={M}: best {best[0]:.3f} us {nbytes / (best[0] * 1e-6) / 1e9:.0f} GB/s {best[1]}")
+            del weights, base
+            torch.cuda.empty_cache()
+
+
+def pick(records, tol=0.005):
+    """Fastest plan; within `tol` of it prefer the persistent grid, no cache hint,
+    fewer rows per wave, smaller blocks (simpler, more robust to other shapes)."""
+    best_us = min(r["us"] for r in records)
+    near = [r for r in records if r["us"] <= best_us * (1 + tol)]
+    near.sort(key=lambda r: (r["plan"]["grid_blocks"] != 0, r["plan"]["nontemporal"],
+                             r["plan"]["rows_per_wave"], r["plan"]["threads_per_block"], r["us"]))
+    return near[0]
+
+
+def emit_inc(path, out=INC_PATH):
+    recs = {}
+    with open(path) as f:
+        for line in f:
+            r = json.loads(line)
+            if "plan" not in r:
+                continue
+            recs.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+    lines = [
+        "// Tuned launch plans for gfx950, one line per (N, K, M):",
+        "//   {N, K, M, {kind, threads_per_block, lanes_per_row, chunks, rows_per_wave, k_split,",
+        "//            nontemporal, grid_blocks}},",
+        "// Generated by `python -m bf16_skinny_gemm_amd.sweep --emit-inc` from an on-device sweep",
+        "// (MI355X, weights rotated over >= 1 GiB of copies, hipGraph replay). Do not edit by hand.",
+    ]
+    for (N, K, M) in sorted(recs):
+        r = pick(recs[(N, K, M)])
+        p = r["plan"]
+        fields = ", ".join(str(p[k]) for k in ("kind", "threads_per_block", "lanes_per_row", "chunks",
+                                               "rows_per_wave", "k_split", "nontemporal", "grid_blocks"))
+        lines.append(f"{{{N}, {K}, {M}, {{{fields}}}}},  // {r['us']:.3f} us, {r['gbps']:.0f} GB/s")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--out", help="JSON-lines file to append measurements to")
+    ap.add_argument("--emit-inc", metavar="JSONL", help="write the plan table from a sweep file")
+    ap.add_argument("--inc-path", default=INC_PATH)
+    ap.add_argument("--only", help="comma list of NxK shapes to sweep")
+    ap.add_argument("--ms", default=",".join(str(m) for m in MS))
+    ap.add_argument("--trials", type=int, default=3)
+    ap.add_argument("--replays", type=int, default=5)
+    args = ap.parse_args()
+    if args.emit_inc:
+        print(emit_inc(args.emit_inc, args.inc_path))
+        return 0
+    if not args.out:
+        ap.error("--out or --emit-inc is required")
+    measure(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.path.insert(0, os.path.dirname(HERE))
+    sys.exit(main())

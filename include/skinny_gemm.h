@@ -1,0 +1,150 @@
+/*
+ * skinny_gemm.h -- C ABI of the MI355X (gfx950) BF16 skinny GEMM library
+ * (libskinny_gemm_bf16.so).
+ *
+ * The operation, F.linear on bfloat16 at decode token counts:
+ *
+ *     y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),   m < M, n < N, k < K,
+ *
+ * with float32 accumulation and one round-to-nearest-even step to bfloat16 at
+ * the end. It is the skinny GEMM of the vLLM pull requests "GLM-5.3-Flash
+ * skinny GEMM plans for SM121" (Overview and Claims: BF16 attention, shared-
+ * expert and LM-head projections at M = 1/2/4, compared against F.linear in
+ * section Validation) and "SM90 skinny GEMM plans" (Overview: 1..4 tokens;
+ * Details: one launch per GEMM, no separate reduce kernel). The paired entry
+ * point is the batched f_b_proj / g_b_proj projection of the vLLM pull request
+ * "Batch paired KDA gate projections" (section "Purpose and source": two
+ * same-shape BF16 projections in one batched call).
+ *
+ * Conventions shared by every entry point below:
+ *  - Pointers x, W, y are DEVICE pointers to bfloat16 values stored as raw
+ *    16-bit patterns. Layouts are row-major and contiguous: x is [M][K], W is
+ *    [N][K] (the nn.Linear weight layout, one output feature per row), y is
+ *    [M][N]. No bias, no scaling.
+ *  - The caller owns every buffer. The library never allocates, frees or
+ *    synchronises in a compute call; it enqueues exactly one kernel on
+ *    `stream` (0 = the null stream) and returns. Calls are therefore legal
+ *    inside HIP graph capture. y must not overlap x or W (or, for the pair,
+ *    each other).
+ *  - Sizes: 0 <= M <= 4; N >= 0; K >= 0. M == 0 or N == 0 is a no-op that
+ *    returns SKINNY_OK (pointers may then be NULL). K == 0 writes +0 to all of
+ *    y (the empty sum). M > 4 is outside the method's decode range and is
+ *    rejected with SKINNY_ERR_INVALID_ARG; the caller keeps its general GEMM.
+ *  - Fast path: x and W 16-byte aligned and K % 8 == 0 (128-bit weight
+ *    loads). Any other alignment or K runs a correct element-wise path; it is
+ *    not an error.
+ *  - Errors are returned, never raised or aborted: arguments are validated
+ *    before anything is enqueued, and nothing is written on error. Only
+ *    gfx950 devices are supported (others: SKINNY_ERR_UNSUPPORTED).
+ *  - Results are deterministic: the same inputs and plan give the same bits on
+ *    every call, eagerly or replayed from a graph. The reduction order depends
+ *    only on the plan's (lanes_per_row, chunks, k_split) and K, so plans that
+ *    share those give identical bits, and the pair gives the same bits as two
+ *    single calls with the same plan.
+ *  - Thread safety: every entry point may be called from any host thread; the
+ *    only shared state is a per-device property cache filled once.
+ */
+#ifndef SKINNY_GEMM_H
+#define SKINNY_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning entry point. */
+typedef enum skinny_status {
+    SKINNY_OK = 0,
+    SKINNY_ERR_INVALID_ARG = -1,     /* null pointer, size out of range, overlap, bad plan */
+    SKINNY_ERR_UNSUPPORTED = -2,     /* no usable device, device is not gfx950, or no compiled
+                                        variant matches the requested plan */
+    SKINNY_ERR_NOT_INITIALIZED = -3, /* reserved: no entry point currently needs prior init */
+    SKINNY_ERR_LAUNCH = -4           /* the HIP runtime refused the launch */
+} skinny_status_t;
+
+/* Kernel families a plan can name. */
+typedef enum skinny_kind {
+    SKINNY_KIND_FIXED_K = 1, /* K fixed at compile time = k_split*lanes_per_row*8*chunks;
+                                x held in registers */
+    SKINNY_KIND_LOOP_K = 2,  /* any K % 8 == 0; x staged in LDS; chunks = loads in flight per row */
+    SKINNY_KIND_SCALAR = 3   /* any K, any alignment; element-wise loads */
+} skinny_kind_t;
+
+/* One launch configuration ("plan"): the knobs of the pages' plan tuple
+ * (block size, outputs per block, K unroll, vector width, static K; vLLM SM121
+ * plan page, section Details) recast for 64-wide wavefronts. Vector width is
+ * fixed at 8 bfloat16 (one 128-bit load per lane). */
+typedef struct skinny_plan {
+    int32_t kind;              /* skinny_kind_t */
+    int32_t threads_per_block; /* 64 * waves per block */
+    int32_t lanes_per_row;     /* lanes sharing one W row in a load instruction: 8, 16, 32, 64 */
+    int32_t chunks;            /* FIXED_K: 16-byte loads per lane per row; LOOP_K: loads per
+                                  lane per row kept in flight (K unroll) */
+    int32_t rows_per_wave;     /* row groups a wave processes per tile (outputs per wave =
+                                  rows_per_wave * 64 / lanes_per_row) */
+    int32_t k_split;           /* waves of one block that split a row's K range (1, 2, 4);
+                                  partial sums meet in LDS, summed in fixed order */
+    int32_t nontemporal;       /* 1: W is read with the non-temporal cache hint */
+    int32_t grid_blocks;       /* 0: a persistent grid that fills the device once (compute
+                                  units x blocks resident per unit), each block looping over
+                                  tiles; > 0: at most this many blocks (a value >= the tile
+                                  count gives one block per tile) */
+} skinny_plan_t;
+
+/* Checks that `device` is a gfx950 GPU and caches its properties. Optional:
+ * every compute call performs the same check lazily on the current device.
+ * Idempotent. Returns SKINNY_OK, SKINNY_ERR_INVALID_ARG (no such device) or
+ * SKINNY_ERR_UNSUPPORTED (not gfx950). */
+int skinny_gemm_init(int device);
+
+/* y = x . W^T with the plan the library's table holds for (N, K, M) on this
+ * architecture, or its default plan when the table has no entry. The table is
+ * keyed like the pages' plan tables: architecture + local (N, K) + M (vLLM SM90
+ * plan page, section Details). */
+int skinny_gemm_bf16(const void *x, const void *W, void *y,
+                     int M, int N, int K, hipStream_t stream);
+
+/* The paired projection: y0 = x . W0^T and y1 = x . W1^T, both [N][K] weights
+ * applied to the one shared x, in ONE kernel launch (vLLM "Batch paired KDA
+ * gate projections", section "Purpose and source"; the batched f_b/g_b row of
+ * the LMDeploy GLM-5.3 page's operator-level gains table). Same conventions as
+ * skinny_gemm_bf16; y0 and y1 must not overlap each other, x, W0 or W1. */
+int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1,
+                          void *y0, void *y1, int M, int N, int K, hipStream_t stream);
+
+/* As skinny_gemm_bf16 / _pair, with an explicit plan (used by the plan sweep
+ * and by tests). The plan must name a compiled variant (see
+ * skinny_gemm_num_variants) compatible with K: for FIXED_K, K must equal
+ * k_split*lanes_per_row*8*chunks. A FIXED_K or LOOP_K plan given misaligned
+ * pointers or K % 8 != 0 returns SKINNY_ERR_INVALID_ARG. grid_blocks may be
+ * any value >= 0 for any variant. */
+int skinny_gemm_bf16_ex(const void *x, const void *W, void *y,
+                        int M, int N, int K, const skinny_plan_t *plan, hipStream_t stream);
+int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1,
+                             void *y0, void *y1, int M, int N, int K,
+                             const skinny_plan_t *plan, hipStream_t stream);
+
+/* The plan skinny_gemm_bf16 would use for (N, K, M) with 16-byte aligned
+ * pointers. Writes *out; returns 1 if it comes from the tuned table, 0 if it is
+ * the default plan, or SKINNY_ERR_INVALID_ARG. Host-only: needs no device. */
+int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out);
+
+/* Enumerates the compiled variants (grid_blocks = 0 in each). Every variant is
+ * compiled for M = 1..4. skinny_gemm_get_variant returns SKINNY_OK or
+ * SKINNY_ERR_INVALID_ARG for an index out of range. Host-only. */
+int skinny_gemm_num_variants(void);
+int skinny_gemm_get_variant(int index, skinny_plan_t *out);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *skinny_gemm_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int skinny_gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_GEMM_H */

@@ -1,0 +1,235 @@
+"""C-ABI contract of libskinny_gemm_bf16.so, checked without running any kernel.
+
+Argument validation happens before the library touches a device, so the
+error paths are exercised here on the CPU with fake (never dereferenced)
+pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+@pytest.fixture(scope="module")
+def skg():
+    from bf16_skinny_gemm_amd.build import LIB_PATH
+
+    if not os.path.exists(LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    import bf16_skinny_gemm_amd
+
+    bf16_skinny_gemm_amd.lib()
+    return bf16_skinny_gemm_amd
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(HEADER_DIR, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(skinny_\w+)\s*\(", text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for want in ("skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",
+                 "skinny_gemm_bf16_pair_ex", "skinny_gemm_init", "skinny_gemm_get_plan",
+                 "skinny_gemm_num_variants", "skinny_gemm_get_variant",
+                 "skinny_gemm_status_string", "skinny_gemm_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(skg):
+    L = skg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in include/ but not exported"
+
+
+def test_exports_have_c_linkage(skg):
+    from bf16_skinny_gemm_amd.build import LIB_PATH
+
+    # C symbols are plain names in the dynamic symbol table (no C++ mangling)
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
+                         text=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms
+
+
+def test_status_strings(skg):
+    for st, tag in ((0, "SKINNY_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED"),
+                    (-3, "NOT_INITIALIZED"), (-4, "LAUNCH"), (12345, "UNKNOWN")):
+        assert tag in skg.skinny_gemm_status_string(st)
+
+
+def test_version(skg):
+    assert skg.skinny_gemm_version() >= 100
+
+
+def test_variants_enumerate(skg):
+    n = skg.skinny_gemm_num_variants()
+    assert n > 10
+    kinds = set()
+    for i in range(n):
+        p = skg.skinny_gemm_get_variant(i)
+        kinds.add(p.kind)
+        assert p.threads_per_block % 64 == 0 and p.grid_blocks == 0
+        assert p.lanes_per_row in (8, 16, 32, 64)
+        assert p.k_split in (1, 2, 4)
+    assert kinds == {1, 2, 3}
+    with pytest.raises(skg.SkinnyError):
+        skg.skinny_gemm_get_variant(n)
+    with pytest.raises(skg.SkinnyError):
+        skg.skinny_gemm_get_variant(-1)
+
+
+def _fixed_k(p):
+    return p.k_split * p.lanes_per_row * 8 * p.chunks
+
+
+def test_default_plans(skg):
+    # every K of the decode projections has a compile-time-K default at every M
+    for (N, K) in [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536),
+                   (4096, 8192), (77440, 4096), (4096, 128)]:
+        for M in (1, 2, 3, 4):
+            p, _ = skg.skinny_gemm_get_plan(N, K, M)
+            assert p.kind == skg.SKINNY_KIND_FIXED_K, (N, K, M, p)
+            assert _fixed_k(p) == K
+    p, tuned = skg.skinny_gemm_get_plan(100, 1000, 2)
+    assert p.kind == skg.SKINNY_KIND_LOOP_K and not tuned
+    p, _ = skg.skinny_gemm_get_plan(100, 1001, 2)
+    assert p.kind == skg.SKINNY_KIND_SCALAR
+
+
+def test_plan_table_entries_are_valid(skg):
+    """Every tuned entry names a compiled variant compatible with its K."""
+    inc = os.path.join(ROOT, "bf16_skinny_gemm_amd", "csrc", "plans_gfx950.inc")
+    rows = re.findall(r"^\s*\{\s*(\d+),\s*(\d+),\s*(\d+),\s*\{([^}]*)\}\s*\},", open(inc).read(), re.M)
+    keys = set()
+    vset = {tuple(v.as_dict()[k] for k in ("kind", "lanes_per_row", "chunks", "rows_per_wave",
+                                           "k_split", "nontemporal"))
+            for v in skg.variants()}
+    for N, K, M, fields in rows:
+        N, K, M = int(N), int(K), int(M)
+        assert (N, K, M) not in keys, f"duplicate plan key {(N, K, M)}"
+        keys.add((N, K, M))
+        p, tuned = skg.skinny_gemm_get_plan(N, K, M)
+        assert tuned
+        vals = [int(v) for v in fields.split(",")]
+        assert vals == [p.kind, p.threads_per_block, p.lanes_per_row, p.chunks, p.rows_per_wave,
+                        p.k_split, p.nontemporal, p.grid_blocks]
+        assert (p.kind, p.lanes_per_row, p.chunks, p.rows_per_wave, p.k_split, p.nontemporal) in vset
+        if p.kind == skg.SKINNY_KIND_FIXED_K:
+            assert _fixed_k(p) == K
+        assert 1 <= M <= 4 and p.threads_per_block // 64 % p.k_split == 0
+
+
+def test_get_plan_rejects(skg):
+    for args in ((0, 128, 1), (128, 0, 1), (128, 128, 0), (128, 128, 5)):
+        with pytest.raises(skg.SkinnyError):
+            skg.skinny_gemm_get_plan(*args)
+    L = skg.lib()
+    assert L.skinny_gemm_get_plan(128, 128, 1, None) == skg.SKINNY_ERR_INVALID_ARG
+
+
+# --- validation before any device work (fake addresses, never dereferenced) ---
+
+X = 0x7F0000000000
+W = 0x7F0000100000
+Y = 0x7F0000900000
+W1 = 0x7F0001000000
+Y1 = 0x7F0002000000
+
+
+def _call(L, *a):
+    return L.skinny_gemm_bf16(*a)
+
+
+@pytest.mark.parametrize("args", [
+    (X, W, Y, 5, 16, 16, None),          # M > 4
+    (X, W, Y, -1, 16, 16, None),         # negative M
+    (X, W, Y, 1, -3, 16, None),          # negative N
+    (X, W, Y, 1, 16, -8, None),          # negative K
+    (None, W, Y, 1, 16, 16, None),       # null x
+    (X, None, Y, 1, 16, 16, None),       # null W
+    (X, W, None, 1, 16, 16, None),       # null y
+    (X + 1, W, Y, 1, 16, 16, None),      # odd address
+    (X, W, X + 8, 1, 16, 16, None),      # y overlaps x
+    (X, W, W + 64, 2, 16, 16, None),     # y overlaps W
+])
+def test_single_invalid_args(skg, args):
+    assert _call(skg.lib(), *args) == skg.SKINNY_ERR_INVALID_ARG
+
+
+def test_pair_invalid_args(skg):
+    L = skg.lib()
+    ok = (X, W, W1, Y, Y1, 1, 16, 16, None)
+    bad = [
+        (X, W, None, Y, Y1, 1, 16, 16, None),   # null W1
+        (X, W, W1, Y, None, 1, 16, 16, None),   # null y1
+        (X, W, W1, Y, Y + 16, 1, 16, 16, None),  # y0 and y1 overlap
+        (X, W, W1, Y, W1 + 32, 1, 16, 16, None),  # y1 overlaps W1
+        (X, W, W1, Y, Y1, 7, 16, 16, None),     # M out of range
+    ]
+    for b in bad:
+        assert L.skinny_gemm_bf16_pair(*b) == skg.SKINNY_ERR_INVALID_ARG, b
+    assert ok  # the valid form needs a device; it is exercised by the GPU tests
+
+
+def test_empty_calls_are_noops(skg):
+    L = skg.lib()
+    # M == 0 or N == 0: nothing to do, any pointers (even NULL) accepted, no device needed
+    assert L.skinny_gemm_bf16(None, None, None, 0, 16, 16, None) == skg.SKINNY_OK
+    assert L.skinny_gemm_bf16(None, None, None, 2, 0, 16, None) == skg.SKINNY_OK
+    assert L.skinny_gemm_bf16_pair(None, None, None, None, None, 0, 4, 4, None) == skg.SKINNY_OK
+
+
+def test_ex_rejects_bad_plans(skg):
+    L = skg.lib()
+    Plan = skg.Plan
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, None, None) == skg.SKINNY_ERR_INVALID_ARG
+    # a plan that names no compiled variant
+    p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=7, rows_per_wave=1,
+             k_split=1, nontemporal=0, grid_blocks=0)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) == \
+        skg.SKINNY_ERR_UNSUPPORTED
+    # compiled variant, wrong K for a fixed-K plan
+    p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
+             k_split=1, nontemporal=0, grid_blocks=0)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 2048, ctypes.byref(p), None) == \
+        skg.SKINNY_ERR_INVALID_ARG
+    # block size not a multiple of 64 * k_split, too large, negative grid
+    for tpb, ks, ch, grid in ((96, 1, 2, 0), (1024, 1, 2, 0), (64, 2, 1, 0), (256, 1, 2, -1)):
+        p = Plan(kind=1, threads_per_block=tpb, lanes_per_row=64, chunks=ch, rows_per_wave=1,
+                 k_split=ks, nontemporal=0, grid_blocks=grid)
+        assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) == \
+            skg.SKINNY_ERR_INVALID_ARG, (tpb, ks, grid)
+    # a vector plan on a misaligned pointer or K % 8 != 0 is an error, not a silent fallback
+    p = Plan(kind=2, threads_per_block=256, lanes_per_row=64, chunks=4, rows_per_wave=1,
+             k_split=1, nontemporal=0, grid_blocks=0)
+    assert L.skinny_gemm_bf16_ex(X + 2, W, Y, 1, 16, 1000, ctypes.byref(p), None) == \
+        skg.SKINNY_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")
+def test_no_device(skg):
+    L = skg.lib()
+    # with no GPU present, a valid call cannot run and says so instead of crashing
+    st = L.skinny_gemm_bf16(X, W, Y, 1, 16, 16, None)
+    assert st in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
+    assert L.skinny_gemm_init(0) in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
+    assert L.skinny_gemm_init(-1) == skg.SKINNY_ERR_INVALID_ARG
