@@ -15,6 +15,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -61,7 +62,62 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run plain device copies of 256 MiB (PMC counter calibration)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("bf16_skinny_gemm_amd/csrc/kernels.hpp", "bf16_skinny_gemm_amd/csrc/skinny_gemm.hip",
+                  "bf16_skinny_gemm_amd/csrc/plans_gfx950.inc")
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources and plan table: PMC records taken on other
+    sources no longer describe the kernels that run."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from profiles/traffic_<workload>.txt, scaled
+    by the plain-copy calibration, or None if absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    try:
+        if rec.get("source_digest") != source_digest() or rec.get("kernel") != kernel:
+            return None
+        fetch = float(rec["fetch_kib_per_dispatch"]) * 1024 * float(rec["copy_fetch_factor"])
+        write = float(rec["write_kib_per_dispatch"]) * 1024 * float(rec["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return round(fetch + write)
+
+
+def copy_calibration() -> int:
+    """Plain device-to-device copies of a known size, for scaling FETCH_SIZE and
+    WRITE_SIZE: each copy reads and writes exactly 256 MiB."""
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 4}), flush=True)
+    return 0
 
 
 def bytes_per_call(cell) -> int:
@@ -78,6 +134,18 @@ def cell_name(cell) -> str:
     return f"({cell[0]},{cell[1]})M{cell[2]}"
 
 
+def kernel_name(p, M) -> str:
+    """The kernel instance a plan launches, spelled as rocprofv3 prints it."""
+    nt = "true" if p.nontemporal else "false"
+    if p.kind == 1:
+        xl = "true" if p.x_in_lds else "false"
+        return (f"void skg::fixed_k_kernel<{M}, {p.lanes_per_row}, {p.chunks}, {p.rows_per_wave}, "
+                f"{p.k_split}, {xl}, {nt}>(skg::Args)")
+    if p.kind == 2:
+        return f"void skg::loop_k_kernel<{M}, {p.chunks}, {p.rows_per_wave}, {nt}>(skg::Args, int)"
+    return f"void skg::scalar_kernel<{M}>(skg::Args, int)"
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -86,6 +154,9 @@ def main() -> int:
               "(the GEMV shards by output rows with no exchange; see DESIGN.md). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch
@@ -225,21 +296,40 @@ def main() -> int:
                "us_min": round(min(per_call), 3), "us_max": round(max(per_call), 3),
                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                "bytes_per_call": b, "calls_per_replay": c["calls"]}
-        if c["cell"][0] != "pair":
+        if c["cell"][0] == "pair":
+            _, N, K, M = c["cell"]
+        else:
             N, K, M = c["cell"]
-            p, tuned = skg.skinny_gemm_get_plan(N, K, M)
-            row["plan"] = p.as_dict()
-            row["tuned_plan"] = tuned
+        p, tuned = skg.skinny_gemm_get_plan(N, K, M)
+        row["plan"] = p.as_dict()
+        row["tuned_plan"] = tuned
+        row["kernel"] = kernel_name(p, M)
         cell_rows.append(row)
         log(f"cell {row['cell']}: {us:.3f} us/call, {gbps:.1f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
         del g
 
-    # the dominant kernel: the cell moving the most bytes per launch (first such cell)
-    dom = max(cell_rows, key=lambda r: (r["bytes_per_call"], -cell_rows.index(r)))
-    roofline = {"bound": "hbm", "kernel": dom["cell"], "achieved": dom["gbps"],
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(dom["gbps"] / PEAK_HBM_GBPS, 4), "traffic": None,
-                "avg_launch_us": dom["us_per_call"], "algorithmic_bytes_per_launch": dom["bytes_per_call"]}
+    # The dominant kernel: the compiled kernel instance that takes the largest share
+    # of the step. Cells that launch the same instance are pooled, so the average
+    # launch duration here is the one rocprofv3 --stats reports for that kernel name.
+    pooled = {}
+    for c, row in zip(cells, cell_rows):
+        key = row.get("kernel", row["cell"])
+        p = pooled.setdefault(key, {"us": 0.0, "launches": 0, "bytes": 0, "cells": []})
+        p["us"] += row["us_per_call"] * c["calls"]
+        p["launches"] += c["calls"]
+        p["bytes"] += row["bytes_per_call"] * c["calls"]
+        p["cells"].append(row["cell"])
+    dom_name, dom = max(pooled.items(), key=lambda kv: kv[1]["us"])
+    avg_us = dom["us"] / dom["launches"]
+    bytes_per_launch = dom["bytes"] / dom["launches"]
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom_name, "cells": dom["cells"],
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": recorded_traffic(args.workload, dom_name),
+                "avg_launch_us": round(avg_us, 3), "launches_per_step": dom["launches"],
+                "algorithmic_bytes_per_launch": round(bytes_per_launch),
+                "share_of_step": round(dom["us"] / sum(p["us"] for p in pooled.values()), 4)}
 
     # ---------------- parity spot check of the timed buffers ----------------
     parity = None
@@ -279,7 +369,7 @@ def main() -> int:
         done_bytes = 0
         t_cpu = 0.0
         passes = 0
-        while t_cpu < args.cpu_seconds and passes < 50:
+        while t_cpu < args.cpu_seconds and passes < 100000:
             for c in cells:
                 cell = c["cell"]
                 t1 = time.perf_counter()
@@ -311,7 +401,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": desc, "launches_per_step": step_calls,
                    "bytes_per_step": step_bytes, "rotation_bytes_min": ROTATE_BYTES,
-                   "accumulate": "fp32", "device": props.name},
+                   "accumulate": "fp32", "device": props.name,
+                   "source_digest": source_digest()},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cells": cell_rows,

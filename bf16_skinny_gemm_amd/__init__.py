@@ -56,6 +56,7 @@ class Plan(ctypes.Structure):
         ("k_split", ctypes.c_int32),
         ("nontemporal", ctypes.c_int32),
         ("grid_blocks", ctypes.c_int32),
+        ("x_in_lds", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -133,27 +133,66 @@ struct Args {
 };
 
 // ---------------------------------------------------------------------------
-// Family FIXED_K: K = KW * LPR * 8 * CH known at compile time, x in registers.
+// Family FIXED_K: K = KW * LPR * 8 * CH known at compile time.
 //
 // A block has W waves (a launch-time value, W % KW == 0) in W/KW groups; the
 // KW waves of a group share the same rows and split K into KW slices. A tile
 // is the rows the block covers per iteration, (W/KW) * ROWS_W consecutive
-// rows; each group owns ROWS_W = R * 64/LPR of them.
-// Lane (sub, kl) = (lane / LPR, lane % LPR) reads, for row r*RPI + sub of its
-// group and chunk j < CH, the 8 elements starting at
-//     kw * K/KW + j * LPR*8 + kl * 8.
+// rows; each group owns ROWS_W = R * 64/LPR of them. Lane (sub, kl) =
+// (lane / LPR, lane % LPR) reads, for row r*RPI + sub of its group and chunk
+// j < CH, the 8 elements starting at  kw * K/KW + j * LPR*8 + kl * 8.
+//
+// x lives in registers (XL = false: each lane keeps the M*CH 16-byte pieces it
+// multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
+// chunk reads its piece back, which frees VGPRs at M = 3, 4).
+//
+// Blocks loop over tiles tile = blockIdx.x, + gridDim.x, ... and software-
+// pipeline them: the loads of the next tile are issued before the current one
+// is consumed, so a wave pays the HBM latency once rather than once per tile.
+// A prefetch past the last tile uses an empty buffer resource and moves no data.
 // ---------------------------------------------------------------------------
 constexpr int kMaxWaves = 8;  // largest block: 512 threads
 
-template <int M, int LPR, int CH, int R, int KW, bool NT>
-__global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
-{
-    constexpr int K = KW * LPR * 8 * CH;
-    constexpr int KSLICE = K / KW;
-    constexpr int RPI = 64 / LPR;
-    constexpr int ROWS_W = R * RPI;
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
+struct FixedK {
+    static constexpr int K = KW * LPR * 8 * CH;
+    static constexpr int KSLICE = K / KW;
+    static constexpr int RPI = 64 / LPR;
+    static constexpr int ROWS_W = R * RPI;
     static_assert(64 % LPR == 0 && LPR >= 8, "lanes per row: 8, 16, 32 or 64");
     static_assert(kMaxWaves % KW == 0, "k_split must divide the largest block");
+
+    // Issue the weight loads of `tile` for this wave's rows.
+    static __device__ __forceinline__ void issue(const Args &a, int tile, int rows_t, int grp,
+                                                 int sub, unsigned kbase, u32x4 (&wv)[R][CH])
+    {
+        const uint16_t *base = a.w0;
+        int valid = 0;
+        if (tile < a.total_tiles) {
+            const int mat = tile >= a.tiles_per_mat ? 1 : 0;
+            const int row0 = (tile - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+            valid = a.N - row0;
+            valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
+            base = (mat ? a.w1 : a.w0) + (size_t)row0 * K;
+        }
+        const __amdgpu_buffer_rsrc_t ws = make_rsrc(base, (unsigned)(valid * K * 2));
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int j = 0; j < CH; ++j)
+                wv[r][j] = load16<NT>(ws, ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u);
+    }
+};
+
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
+__global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
+{
+    using F = FixedK<M, LPR, CH, R, KW, XL, NT>;
+    constexpr int K = F::K;
+    constexpr int KSLICE = F::KSLICE;
+    constexpr int RPI = F::RPI;
+    constexpr int ROWS_W = F::ROWS_W;
+    constexpr int OUT = sum_lane<LPR>();
 
     // The host launches blockDim.x = 64 * waves with waves % KW == 0.
     const int groups = (int)(blockDim.x >> 6) / KW;
@@ -165,51 +204,67 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     const int sub = lane / LPR;
     const int kl = lane % LPR;
     const unsigned kbase = (unsigned)(kw * KSLICE + kl * 8);
+    const int step = (int)gridDim.x;
 
-    // This lane's K positions of every x row.
-    u32x4 xr[M][CH];
+    int tile = blockIdx.x;
+    if (tile >= a.total_tiles)
+        return;  // whole block
+
+    u32x4 wa[R][CH], wb[R][CH];
+    F::issue(a, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
+
+    __shared__ u32x4 x_lds[XL ? M * K / 8 : 1];
+    __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
+    u32x4 xr[XL ? 1 : M][XL ? 1 : CH];
     {
         const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+        if constexpr (XL) {
+            for (int i = threadIdx.x; i < M * K / 8; i += (int)blockDim.x)
+                x_lds[i] = load16<false>(xs, (unsigned)i * 16u);
+            __syncthreads();
+        } else {
 #pragma unroll
-        for (int m = 0; m < M; ++m)
+            for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int j = 0; j < CH; ++j)
-                xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
+                for (int j = 0; j < CH; ++j)
+                    xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
+        }
     }
 
-    __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
-
-    for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
-        const int mat = tile >= a.tiles_per_mat ? 1 : 0;
-        const int t = tile - mat * a.tiles_per_mat;
-        const uint16_t *wm = mat ? a.w1 : a.w0;
-        uint16_t *ym = mat ? a.y1 : a.y0;
-        const int row0 = t * rows_t + grp * ROWS_W;
-        int valid = a.N - row0;
-        valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
-        const __amdgpu_buffer_rsrc_t ws =
-            make_rsrc(wm + (size_t)row0 * K, (unsigned)(valid * K * 2));
-
-        u32x4 wv[R][CH];
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int j = 0; j < CH; ++j)
-                wv[r][j] = load16<NT>(ws, ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u);
-
+    auto consume = [&](int t, const u32x4 (&wv)[R][CH]) {
         float acc[M][R];
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float s = 0.0f;
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = 0.0f;
 #pragma unroll
-                for (int j = 0; j < CH; ++j)
-                    s = dot8(wv[r][j], xr[m][j], s);
-                acc[m][r] = group_sum<LPR>(s);
+        for (int j = 0; j < CH; ++j)
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                u32x4 xv;
+                if constexpr (XL) {
+                    // volatile: keep the LDS read here; hoisting it out of the tile
+                    // loop would rebuild the register copy of x that XL avoids
+                    const volatile __attribute__((address_space(3))) u32x4 *xp =
+                        (const volatile __attribute__((address_space(3))) u32x4 *)x_lds;
+                    xv = xp[(m * K + (int)kbase + j * LPR * 8) / 8];
+                } else {
+                    xv = xr[m][j];
+                }
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[m][r] = dot8(wv[r][j], xv, acc[m][r]);
             }
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = group_sum<LPR>(acc[m][r]);
 
-        constexpr int OUT = sum_lane<LPR>();
+        const int mat = t >= a.tiles_per_mat ? 1 : 0;
+        uint16_t *ym = mat ? a.y1 : a.y0;
+        const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
         if constexpr (KW == 1) {
             if (kl == OUT) {
 #pragma unroll
@@ -249,6 +304,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
             }
             __syncthreads();
         }
+    };
+
+    // Two register sets alternate: while one tile is consumed, the next is in flight.
+    while (true) {
+        F::issue(a, tile + step, rows_t, grp, sub, kbase, wb);
+        consume(tile, wa);
+        tile += step;
+        if (tile >= a.total_tiles)
+            break;
+        F::issue(a, tile + step, rows_t, grp, sub, kbase, wa);
+        consume(tile, wb);
+        tile += step;
+        if (tile >= a.total_tiles)
+            break;
     }
 }
 

@@ -31,28 +31,31 @@ struct Variant {
     int rows_per_group;    // rows one wave group covers per tile
 };
 
-// Register budget per lane: x slice 4*M*CH VGPRs (at most 128) plus weight
-// loads in flight 4*R*CH, together at most 192, so no instance spills.
-constexpr bool fits(int M, int CH, int R) { return M * CH <= 32 && CH * (M + R) <= 48; }
+// Register budget per lane, so that no instance spills: x in registers takes
+// 4*M*CH VGPRs (at most 128), the two alternating weight sets 2*4*R*CH.
+constexpr bool fits(int M, int CH, int R, bool XL)
+{
+    return XL ? R * CH <= 20 : (M * CH <= 32 && CH * (M + 2 * R) <= 48);
+}
 
-template <int M, int LPR, int CH, int R, int KW, bool NT>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
 constexpr const void *fixed_fn()
 {
-    if constexpr (fits(M, CH, R))
-        return reinterpret_cast<const void *>(&skg::fixed_k_kernel<M, LPR, CH, R, KW, NT>);
+    if constexpr (fits(M, CH, R, XL))
+        return reinterpret_cast<const void *>(&skg::fixed_k_kernel<M, LPR, CH, R, KW, XL, NT>);
     else
         return nullptr;
 }
 
-template <int LPR, int CH, int R, int KW, bool NT>
+template <int LPR, int CH, int R, int KW, bool XL, bool NT>
 Variant fixed_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0};
-    v.fn[0] = fixed_fn<1, LPR, CH, R, KW, NT>();
-    v.fn[1] = fixed_fn<2, LPR, CH, R, KW, NT>();
-    v.fn[2] = fixed_fn<3, LPR, CH, R, KW, NT>();
-    v.fn[3] = fixed_fn<4, LPR, CH, R, KW, NT>();
+    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0};
+    v.fn[0] = fixed_fn<1, LPR, CH, R, KW, XL, NT>();
+    v.fn[1] = fixed_fn<2, LPR, CH, R, KW, XL, NT>();
+    v.fn[2] = fixed_fn<3, LPR, CH, R, KW, XL, NT>();
+    v.fn[3] = fixed_fn<4, LPR, CH, R, KW, XL, NT>();
     v.k_fixed = KW * LPR * 8 * CH;
     v.rows_per_group = R * (64 / LPR);
     return v;
@@ -62,7 +65,7 @@ template <int U, int R, bool NT>
 Variant loop_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_LOOP_K, 256, 64, U, R, 1, NT ? 1 : 0, 0};
+    v.plan = skinny_plan_t{SKINNY_KIND_LOOP_K, 256, 64, U, R, 1, NT ? 1 : 0, 0, 1};
     v.fn[0] = reinterpret_cast<const void *>(&skg::loop_k_kernel<1, U, R, NT>);
     v.fn[1] = reinterpret_cast<const void *>(&skg::loop_k_kernel<2, U, R, NT>);
     v.fn[2] = reinterpret_cast<const void *>(&skg::loop_k_kernel<3, U, R, NT>);
@@ -75,7 +78,7 @@ Variant loop_variant()
 Variant scalar_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_SCALAR, 256, 64, 1, 1, 1, 0, 0};
+    v.plan = skinny_plan_t{SKINNY_KIND_SCALAR, 256, 64, 1, 1, 1, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(&skg::scalar_kernel<1>);
     v.fn[1] = reinterpret_cast<const void *>(&skg::scalar_kernel<2>);
     v.fn[2] = reinterpret_cast<const void *>(&skg::scalar_kernel<3>);
@@ -85,19 +88,23 @@ Variant scalar_variant()
     return v;
 }
 
-#define SKG_FIXED_R(LPR, CH, KW, NT)                                                   \
-    fixed_variant<LPR, CH, 1, KW, NT>(), fixed_variant<LPR, CH, 2, KW, NT>(),          \
-        fixed_variant<LPR, CH, 4, KW, NT>()
-#define SKG_FIXED(LPR, CH, KW) SKG_FIXED_R(LPR, CH, KW, false), SKG_FIXED_R(LPR, CH, KW, true)
-// chunks = 16 leaves room for one or two rows in flight only (see fits())
-#define SKG_FIXED16(LPR, KW)                                                                 \
-    fixed_variant<LPR, 16, 1, KW, false>(), fixed_variant<LPR, 16, 2, KW, false>(),          \
-        fixed_variant<LPR, 16, 1, KW, true>(), fixed_variant<LPR, 16, 2, KW, true>()
+// Per (lanes_per_row, chunks, k_split): rows per wave 1, 2, 4 with the
+// non-temporal hint and x in registers or LDS, plus the plain-cached form at
+// one row per wave (the hint won every cell of the gfx950 sweep).
+#define SKG_FIXED(LPR, CH, KW)                                                                       \
+    fixed_variant<LPR, CH, 1, KW, false, true>(), fixed_variant<LPR, CH, 2, KW, false, true>(),      \
+        fixed_variant<LPR, CH, 4, KW, false, true>(), fixed_variant<LPR, CH, 1, KW, true, true>(),   \
+        fixed_variant<LPR, CH, 2, KW, true, true>(), fixed_variant<LPR, CH, 4, KW, true, true>(),    \
+        fixed_variant<LPR, CH, 1, KW, false, false>()
+// chunks = 16 leaves room for one or two rows per wave only (see fits())
+#define SKG_FIXED16(LPR, KW)                                                                         \
+    fixed_variant<LPR, 16, 1, KW, false, true>(), fixed_variant<LPR, 16, 1, KW, true, true>(),       \
+        fixed_variant<LPR, 16, 1, KW, false, false>()
 #define SKG_LOOP(U, R) loop_variant<U, R, false>(), loop_variant<U, R, true>()
 
 // The compiled set. FIXED_K triples (lanes_per_row, chunks, k_split) cover the
 // K of the decode projections: 128 (paired f_b/g_b), 1024, 1536, 4096, 8192.
-const Variant kVariants[] = {
+const Variant kAllVariants[] = {
     // K = 128
     SKG_FIXED(16, 1, 1), SKG_FIXED(8, 2, 1),
     // K = 1024
@@ -113,7 +120,29 @@ const Variant kVariants[] = {
     // any K, any alignment
     scalar_variant(),
 };
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+constexpr int kNumAll = sizeof(kAllVariants) / sizeof(kAllVariants[0]);
+
+// The enumerable set: every entry of kAllVariants that runs at least one M.
+struct Registry {
+    const Variant *v[kNumAll];
+    int n;
+    const Variant *scalar;
+};
+
+const Registry &registry()
+{
+    static const Registry r = [] {
+        Registry q{};
+        for (const Variant &v : kAllVariants) {
+            if (v.fn[0] || v.fn[1] || v.fn[2] || v.fn[3])
+                q.v[q.n++] = &v;
+            if (v.plan.kind == SKINNY_KIND_SCALAR)
+                q.scalar = &v;
+        }
+        return q;
+    }();
+    return r;
+}
 
 // Tuned plans: (N, K, M) -> plan, generated by the on-device sweep.
 struct PlanEntry {
@@ -122,7 +151,7 @@ struct PlanEntry {
 };
 const PlanEntry kPlanTable[] = {
 #include "plans_gfx950.inc"
-    {0, 0, 0, {0, 0, 0, 0, 0, 0, 0, 0}},  // sentinel
+    {0, 0, 0, {0, 0, 0, 0, 0, 0, 0, 0, 0}},  // sentinel
 };
 constexpr int kNumPlans = sizeof(kPlanTable) / sizeof(kPlanTable[0]) - 1;
 
@@ -130,14 +159,15 @@ bool same_variant(const skinny_plan_t &a, const skinny_plan_t &b)
 {
     return a.kind == b.kind && a.lanes_per_row == b.lanes_per_row && a.chunks == b.chunks &&
            a.rows_per_wave == b.rows_per_wave && a.k_split == b.k_split &&
-           a.nontemporal == b.nontemporal;
+           a.nontemporal == b.nontemporal && a.x_in_lds == b.x_in_lds;
 }
 
 const Variant *find_variant(const skinny_plan_t &p)
 {
-    for (int i = 0; i < kNumVariants; ++i)
-        if (same_variant(kVariants[i].plan, p))
-            return &kVariants[i];
+    const Registry &r = registry();
+    for (int i = 0; i < r.n; ++i)
+        if (same_variant(r.v[i]->plan, p))
+            return r.v[i];
     return nullptr;
 }
 
@@ -145,19 +175,18 @@ const Variant *find_variant(const skinny_plan_t &p)
 skinny_plan_t default_plan(int N, int K, int M)
 {
     (void)N;
-    skinny_plan_t p{SKINNY_KIND_LOOP_K, 256, 64, 4, 1, 1, 0, 0};
-    if (K % 8 != 0) {
-        p = kVariants[kNumVariants - 1].plan;
-        return p;
-    }
-    // Prefer a FIXED_K variant for this K with R = 1, no hint, the fewest
-    // k_split waves whose x slice fits the register budget, and for K <= 256
-    // the narrowest row groups (more rows per load).
+    skinny_plan_t p{SKINNY_KIND_LOOP_K, 256, 64, 4, 1, 1, 1, 0, 1};
+    if (K % 8 != 0)
+        return registry().scalar->plan;
+    // Prefer a FIXED_K variant for this K with one row per wave, the
+    // non-temporal hint, x in registers, the fewest k_split waves whose x slice
+    // fits the register budget, and the widest row groups.
     const Variant *best = nullptr;
-    for (int i = 0; i < kNumVariants; ++i) {
-        const Variant &v = kVariants[i];
+    const Registry &reg = registry();
+    for (int i = 0; i < reg.n; ++i) {
+        const Variant &v = *reg.v[i];
         if (v.plan.kind != SKINNY_KIND_FIXED_K || v.k_fixed != K || v.plan.rows_per_wave != 1 ||
-            v.plan.nontemporal != 0 || v.fn[M - 1] == nullptr)
+            v.plan.nontemporal != 1 || v.plan.x_in_lds != 0 || v.fn[M - 1] == nullptr)
             continue;
         if (!best) {
             best = &v;
@@ -299,6 +328,8 @@ int plan_ok(const skinny_plan_t &p, const Variant *v)
         return SKINNY_ERR_INVALID_ARG;
     if (p.kind == SKINNY_KIND_SCALAR && tpb != 256)
         return SKINNY_ERR_INVALID_ARG;
+    if (p.x_in_lds != 0 && p.x_in_lds != 1)
+        return SKINNY_ERR_INVALID_ARG;
     return SKINNY_OK;
 }
 
@@ -307,8 +338,8 @@ hipError_t launch(const void *fn, int grid, int block, size_t lds, void **args, 
     return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, lds, s);
 }
 
-std::atomic<int> g_lds_raised[kNumVariants][4];
-std::atomic<int> g_occupancy[kNumVariants][4][skg::kMaxWaves + 1];
+std::atomic<int> g_lds_raised[kNumAll][4];
+std::atomic<int> g_occupancy[kNumAll][4][skg::kMaxWaves + 1];
 
 // Blocks of this kernel one CU holds at once (cached; 1 if the query fails).
 int blocks_per_cu(int vidx, int M, const void *fn, int tpb, size_t lds)
@@ -374,7 +405,7 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
     if (!vec && plan.kind != SKINNY_KIND_SCALAR) {
         if (plan_in)
             return SKINNY_ERR_INVALID_ARG;
-        plan = kVariants[kNumVariants - 1].plan;
+        plan = registry().scalar->plan;
     }
     if (!plan_in && plan.kind == SKINNY_KIND_FIXED_K) {
         const Variant *v = find_variant(plan);
@@ -394,7 +425,7 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
     a.N = c.N;
     a.K = c.K;
 
-    const int vidx = (int)(v - kVariants);
+    const int vidx = (int)(v - kAllVariants);
     hipError_t err;
     if (plan.kind == SKINNY_KIND_SCALAR) {
         int nmats = c.nmats;
@@ -411,7 +442,7 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         const long long rows_per_tile = (long long)(waves / plan.k_split) * v->rows_per_group;
         const long long tiles = ((long long)c.N + rows_per_tile - 1) / rows_per_tile;
         const long long total = tiles * c.nmats;
-        if (total > 0x7FFFFFFF)
+        if (total > (1LL << 30))  // keeps tile + gridDim.x inside int in the kernels
             return SKINNY_ERR_INVALID_ARG;
         // every buffer resource spans at most one wave group's rows
         if ((long long)v->rows_per_group * c.K * 2 > 0x7FFFFFFFLL)
@@ -440,7 +471,7 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
                 if (plan_in)
                     return SKINNY_ERR_UNSUPPORTED;
                 // x does not fit in LDS: element-wise path
-                const Variant *sv = &kVariants[kNumVariants - 1];
+                const Variant *sv = registry().scalar;
                 int nmats = c.nmats;
                 const long long blocks = ((long long)c.nmats * c.N + 3) / 4;
                 if (blocks > 0x7FFFFFFF)
@@ -510,13 +541,14 @@ int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out)
     return lookup_plan(N, K, M, out) ? 1 : 0;
 }
 
-int skinny_gemm_num_variants(void) { return kNumVariants; }
+int skinny_gemm_num_variants(void) { return registry().n; }
 
 int skinny_gemm_get_variant(int index, skinny_plan_t *out)
 {
-    if (!out || index < 0 || index >= kNumVariants)
+    const Registry &r = registry();
+    if (!out || index < 0 || index >= r.n)
         return SKINNY_ERR_INVALID_ARG;
-    *out = kVariants[index].plan;
+    *out = r.v[index]->plan;
     return SKINNY_OK;
 }
 

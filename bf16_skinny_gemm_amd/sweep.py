@@ -35,6 +35,8 @@ SHAPES = [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536),
 PAIR_SHAPES = [(4096, 128)]
 MS = (1, 2, 3, 4)
 BIG_GRID = 1 << 30  # grid_blocks >= tile count: one block per tile
+PLAN_FIELDS = ("kind", "threads_per_block", "lanes_per_row", "chunks", "rows_per_wave", "k_split",
+               "nontemporal", "grid_blocks", "x_in_lds")
 
 
 def log(msg):
@@ -61,8 +63,7 @@ def candidate_plans(skg, K, M):
 
 def plan_key(p) -> tuple:
     d = p.as_dict()
-    return tuple(d[k] for k in ("kind", "threads_per_block", "lanes_per_row", "chunks",
-                                "rows_per_wave", "k_split", "nontemporal", "grid_blocks"))
+    return tuple(d[k] for k in PLAN_FIELDS)
 
 
 def time_plan(torch, skg, x, weights, ys, plan, pair, trials, replays):
@@ -189,15 +190,14 @@ def emit_inc(path, out=INC_PATH):
     lines = [
         "// Tuned launch plans for gfx950, one line per (N, K, M):",
         "//   {N, K, M, {kind, threads_per_block, lanes_per_row, chunks, rows_per_wave, k_split,",
-        "//            nontemporal, grid_blocks}},",
+        "//            nontemporal, grid_blocks, x_in_lds}},",
         "// Generated by `python -m bf16_skinny_gemm_amd.sweep --emit-inc` from an on-device sweep",
         "// (MI355X, weights rotated over >= 1 GiB of copies, hipGraph replay). Do not edit by hand.",
     ]
     for (N, K, M) in sorted(recs):
         r = pick(recs[(N, K, M)])
         p = r["plan"]
-        fields = ", ".join(str(p[k]) for k in ("kind", "threads_per_block", "lanes_per_row", "chunks",
-                                               "rows_per_wave", "k_split", "nontemporal", "grid_blocks"))
+        fields = ", ".join(str(p.get(k, 0)) for k in PLAN_FIELDS)
         lines.append(f"{{{N}, {K}, {M}, {{{fields}}}}},  // {r['us']:.3f} us, {r['gbps']:.0f} GB/s")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")

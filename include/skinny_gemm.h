@@ -67,7 +67,7 @@ typedef enum skinny_status {
 /* Kernel families a plan can name. */
 typedef enum skinny_kind {
     SKINNY_KIND_FIXED_K = 1, /* K fixed at compile time = k_split*lanes_per_row*8*chunks;
-                                x held in registers */
+                                x in registers or LDS, tiles software-pipelined */
     SKINNY_KIND_LOOP_K = 2,  /* any K % 8 == 0; x staged in LDS; chunks = loads in flight per row */
     SKINNY_KIND_SCALAR = 3   /* any K, any alignment; element-wise loads */
 } skinny_kind_t;
@@ -91,6 +91,9 @@ typedef struct skinny_plan {
                                   units x blocks resident per unit), each block looping over
                                   tiles; > 0: at most this many blocks (a value >= the tile
                                   count gives one block per tile) */
+    int32_t x_in_lds;          /* FIXED_K: 1 = x staged once per block in LDS, 0 = each lane
+                                  keeps its slice of x in registers; LOOP_K: always 1;
+                                  SCALAR: always 0 */
 } skinny_plan_t;
 
 /* Checks that `device` is a gfx950 GPU and caches its properties. Optional:

@@ -102,13 +102,17 @@ def _fixed_k(p):
 
 
 def test_default_plans(skg):
-    # every K of the decode projections has a compile-time-K default at every M
+    # every decode projection shape has a vector plan at every M (tuned or default)
     for (N, K) in [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536),
                    (4096, 8192), (77440, 4096), (4096, 128)]:
         for M in (1, 2, 3, 4):
             p, _ = skg.skinny_gemm_get_plan(N, K, M)
-            assert p.kind == skg.SKINNY_KIND_FIXED_K, (N, K, M, p)
-            assert _fixed_k(p) == K
+            assert p.kind in (skg.SKINNY_KIND_FIXED_K, skg.SKINNY_KIND_LOOP_K), (N, K, M, p)
+            if p.kind == skg.SKINNY_KIND_FIXED_K:
+                assert _fixed_k(p) == K
+    # an unlisted K that a compile-time-K variant covers gets that variant by default
+    p, tuned = skg.skinny_gemm_get_plan(1000, 4096, 1)
+    assert not tuned and p.kind == skg.SKINNY_KIND_FIXED_K and _fixed_k(p) == 4096
     p, tuned = skg.skinny_gemm_get_plan(100, 1000, 2)
     assert p.kind == skg.SKINNY_KIND_LOOP_K and not tuned
     p, _ = skg.skinny_gemm_get_plan(100, 1001, 2)
@@ -121,7 +125,7 @@ def test_plan_table_entries_are_valid(skg):
     rows = re.findall(r"^\s*\{\s*(\d+),\s*(\d+),\s*(\d+),\s*\{([^}]*)\}\s*\},", open(inc).read(), re.M)
     keys = set()
     vset = {tuple(v.as_dict()[k] for k in ("kind", "lanes_per_row", "chunks", "rows_per_wave",
-                                           "k_split", "nontemporal"))
+                                           "k_split", "nontemporal", "x_in_lds"))
             for v in skg.variants()}
     for N, K, M, fields in rows:
         N, K, M = int(N), int(K), int(M)
@@ -131,8 +135,9 @@ def test_plan_table_entries_are_valid(skg):
         assert tuned
         vals = [int(v) for v in fields.split(",")]
         assert vals == [p.kind, p.threads_per_block, p.lanes_per_row, p.chunks, p.rows_per_wave,
-                        p.k_split, p.nontemporal, p.grid_blocks]
-        assert (p.kind, p.lanes_per_row, p.chunks, p.rows_per_wave, p.k_split, p.nontemporal) in vset
+                        p.k_split, p.nontemporal, p.grid_blocks, p.x_in_lds]
+        assert (p.kind, p.lanes_per_row, p.chunks, p.rows_per_wave, p.k_split, p.nontemporal,
+                p.x_in_lds) in vset
         if p.kind == skg.SKINNY_KIND_FIXED_K:
             assert _fixed_k(p) == K
         assert 1 <= M <= 4 and p.threads_per_block // 64 % p.k_split == 0
@@ -212,6 +217,11 @@ def test_ex_rejects_bad_plans(skg):
              k_split=1, nontemporal=0, grid_blocks=0)
     assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 2048, ctypes.byref(p), None) == \
         skg.SKINNY_ERR_INVALID_ARG
+    # x_in_lds must be 0 or 1
+    p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
+             k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=2)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) in \
+        (skg.SKINNY_ERR_INVALID_ARG, skg.SKINNY_ERR_UNSUPPORTED)
     # block size not a multiple of 64 * k_split, too large, negative grid
     for tpb, ks, ch, grid in ((96, 1, 2, 0), (1024, 1, 2, 0), (64, 2, 1, 0), (256, 1, 2, -1)):
         p = Plan(kind=1, threads_per_block=tpb, lanes_per_row=64, chunks=ch, rows_per_wave=1,
@@ -220,7 +230,7 @@ def test_ex_rejects_bad_plans(skg):
             skg.SKINNY_ERR_INVALID_ARG, (tpb, ks, grid)
     # a vector plan on a misaligned pointer or K % 8 != 0 is an error, not a silent fallback
     p = Plan(kind=2, threads_per_block=256, lanes_per_row=64, chunks=4, rows_per_wave=1,
-             k_split=1, nontemporal=0, grid_blocks=0)
+             k_split=1, nontemporal=0, grid_blocks=0, x_in_lds=1)
     assert L.skinny_gemm_bf16_ex(X + 2, W, Y, 1, 16, 1000, ctypes.byref(p), None) == \
         skg.SKINNY_ERR_INVALID_ARG
 

@@ -83,7 +83,7 @@ def _variant_cases():
     except Exception:  # library missing: collected as one failing case
         return [pytest.param(None, id="no-library")]
     return [pytest.param(v, id=f"v{i}-k{v.kind}-l{v.lanes_per_row}-c{v.chunks}-r{v.rows_per_wave}"
-                                f"-s{v.k_split}-nt{v.nontemporal}")
+                                f"-s{v.k_split}-nt{v.nontemporal}-x{v.x_in_lds}")
             for i, v in enumerate(vs)]
 
 
