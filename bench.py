@@ -4,9 +4,9 @@
 One step = one hipGraph replay that runs every (shape, M) cell of the workload,
 each over rotated copies of its weight adding up to at least 1 GiB, so that
 every call streams its weight from HBM rather than from the 256 MB Infinity
-Cache (the cold-cache protocol of the vLLM SM90 plan page, section "How it was
-measured": chains over copies of the weight totalling 1 GiB or more, captured
-in a graph). Inputs are synthetic and seeded (x ~ N(0,1), W ~ N(0,1/K)).
+Cache (the cold-cache protocol of vLLM PR #65306, SM90 skinny GEMM plans,
+section Validation: graph-captured chains over weight copies of 1 GiB or
+more). Inputs are synthetic and seeded (x ~ N(0,1), W ~ N(0,1/K)).
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -139,8 +139,9 @@ def kernel_name(p, M) -> str:
     nt = "true" if p.nontemporal else "false"
     if p.kind == 1:
         xl = "true" if p.x_in_lds else "false"
+        pf = "true" if p.prefetch else "false"
         return (f"void skg::fixed_k_kernel<{M}, {p.lanes_per_row}, {p.chunks}, {p.rows_per_wave}, "
-                f"{p.k_split}, {xl}, {nt}>(skg::Args)")
+                f"{p.k_split}, {xl}, {nt}, {pf}>(skg::Args)")
     if p.kind == 2:
         return f"void skg::loop_k_kernel<{M}, {p.chunks}, {p.rows_per_wave}, {nt}>(skg::Args, int)"
     return f"void skg::scalar_kernel<{M}>(skg::Args, int)"
@@ -150,9 +151,9 @@ def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the GEMV shards by output rows with no exchange; see DESIGN.md). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. "
+              "The GEMV shards by output rows with no exchange, so N GPUs each run one "
+              "rank's share at its own shape; run with --gpus 1.", file=sys.stderr)
         return 2
 
     if args.copy_calibration:

@@ -57,6 +57,7 @@ class Plan(ctypes.Structure):
         ("nontemporal", ctypes.c_int32),
         ("grid_blocks", ctypes.c_int32),
         ("x_in_lds", ctypes.c_int32),
+        ("prefetch", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

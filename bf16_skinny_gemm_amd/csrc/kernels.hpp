@@ -3,9 +3,10 @@
 // y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),  M <= 4 rows of x, W [N][K] row-major.
 //
 // At M <= 4 the product does M flops per weight byte, so its speed is the speed
-// at which W streams out of HBM (the pages' "% of HBM peak = weight bytes /
-// time / peak", vLLM SM90 plan page, section Validation). Everything below is
-// arranged around keeping enough 128-bit weight loads in flight on every CU:
+// at which W streams out of HBM; vLLM PR #65306 (SM90 skinny GEMM plans), section
+// Validation, rates such kernels by weight bytes per second against the HBM
+// peak. Everything below is arranged around keeping enough 128-bit weight loads
+// in flight on every CU:
 //
 //  * a wavefront reads W with raw buffer loads of 16 bytes per lane; the
 //    64 lanes are split into groups of LPR lanes, each group covering one row,
@@ -146,14 +147,16 @@ struct Args {
 // multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
 // chunk reads its piece back, which frees VGPRs at M = 3, 4).
 //
-// Blocks loop over tiles tile = blockIdx.x, + gridDim.x, ... and software-
-// pipeline them: the loads of the next tile are issued before the current one
-// is consumed, so a wave pays the HBM latency once rather than once per tile.
-// A prefetch past the last tile uses an empty buffer resource and moves no data.
+// Blocks loop over tiles tile = blockIdx.x, + gridDim.x, ... With PF the loop
+// is software-pipelined: the loads of the next tile are issued before the
+// current one is consumed, so a wave pays the HBM latency once rather than once
+// per tile; a prefetch past the last tile uses an empty buffer resource and
+// moves no data. Without PF each tile is loaded and then consumed, which keeps
+// one register set and suits grids of one tile per block.
 // ---------------------------------------------------------------------------
 constexpr int kMaxWaves = 8;  // largest block: 512 threads
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
 struct FixedK {
     static constexpr int K = KW * LPR * 8 * CH;
     static constexpr int KSLICE = K / KW;
@@ -184,10 +187,10 @@ struct FixedK {
     }
 };
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
 __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 {
-    using F = FixedK<M, LPR, CH, R, KW, XL, NT>;
+    using F = FixedK<M, LPR, CH, R, KW, XL, NT, PF>;
     constexpr int K = F::K;
     constexpr int KSLICE = F::KSLICE;
     constexpr int RPI = F::RPI;
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     if (tile >= a.total_tiles)
         return;  // whole block
 
-    u32x4 wa[R][CH], wb[R][CH];
+    u32x4 wa[R][CH], wb[PF ? R : 1][PF ? CH : 1];
     F::issue(a, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
 
     __shared__ u32x4 x_lds[XL ? M * K / 8 : 1];
@@ -306,18 +309,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
         }
     };
 
-    // Two register sets alternate: while one tile is consumed, the next is in flight.
-    while (true) {
-        F::issue(a, tile + step, rows_t, grp, sub, kbase, wb);
-        consume(tile, wa);
-        tile += step;
-        if (tile >= a.total_tiles)
-            break;
-        F::issue(a, tile + step, rows_t, grp, sub, kbase, wa);
-        consume(tile, wb);
-        tile += step;
-        if (tile >= a.total_tiles)
-            break;
+    if constexpr (PF) {
+        // Two register sets alternate: while one tile is consumed, the next is in flight.
+        while (true) {
+            F::issue(a, tile + step, rows_t, grp, sub, kbase, wb);
+            consume(tile, wa);
+            tile += step;
+            if (tile >= a.total_tiles)
+                break;
+            F::issue(a, tile + step, rows_t, grp, sub, kbase, wa);
+            consume(tile, wb);
+            tile += step;
+            if (tile >= a.total_tiles)
+                break;
+        }
+    } else {
+        while (true) {
+            consume(tile, wa);
+            tile += step;
+            if (tile >= a.total_tiles)
+                break;
+            F::issue(a, tile, rows_t, grp, sub, kbase, wa);
+        }
     }
 }
 

@@ -1,9 +1,9 @@
 // Host side of libskinny_gemm_bf16.so: compiled variants, the plan table,
 // argument validation and the C ABI declared in include/skinny_gemm.h.
 //
-// Dispatch follows the pages' plan-table design (vLLM SM90 skinny-GEMM plan
-// page, section Details: a table keyed by architecture and local (N, K), per
-// token count M, with a default path for shapes it does not list), rebuilt for
+// Dispatch follows the plan-table design of vLLM PR #65306 (SM90 skinny GEMM
+// plans), section Details: a table keyed by architecture and local (N, K), per
+// token count M, with a default path for shapes it does not list; rebuilt for
 // gfx950: the table holds launch plans of the hand-written kernels in
 // kernels.hpp, and a shape missing from it gets a heuristic default plan
 // instead of a different library.
@@ -32,30 +32,33 @@ struct Variant {
 };
 
 // Register budget per lane, so that no instance spills: x in registers takes
-// 4*M*CH VGPRs (at most 128), the two alternating weight sets 2*4*R*CH.
-constexpr bool fits(int M, int CH, int R, bool XL)
+// 4*M*CH VGPRs (at most 128), the weight sets in flight 4*R*CH each (two with
+// prefetch).
+constexpr bool fits(int M, int CH, int R, bool XL, bool PF)
 {
-    return XL ? R * CH <= 20 : (M * CH <= 32 && CH * (M + 2 * R) <= 48);
+    const int w = (PF ? 2 : 1) * R * CH;
+    return XL ? w <= 20 : (M * CH <= 32 && M * CH + w <= 48);
 }
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
 constexpr const void *fixed_fn()
 {
-    if constexpr (fits(M, CH, R, XL))
-        return reinterpret_cast<const void *>(&skg::fixed_k_kernel<M, LPR, CH, R, KW, XL, NT>);
+    if constexpr (fits(M, CH, R, XL, PF))
+        return reinterpret_cast<const void *>(&skg::fixed_k_kernel<M, LPR, CH, R, KW, XL, NT, PF>);
     else
         return nullptr;
 }
 
-template <int LPR, int CH, int R, int KW, bool XL, bool NT>
+template <int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
 Variant fixed_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0};
-    v.fn[0] = fixed_fn<1, LPR, CH, R, KW, XL, NT>();
-    v.fn[1] = fixed_fn<2, LPR, CH, R, KW, XL, NT>();
-    v.fn[2] = fixed_fn<3, LPR, CH, R, KW, XL, NT>();
-    v.fn[3] = fixed_fn<4, LPR, CH, R, KW, XL, NT>();
+    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0,
+                           PF ? 1 : 0};
+    v.fn[0] = fixed_fn<1, LPR, CH, R, KW, XL, NT, PF>();
+    v.fn[1] = fixed_fn<2, LPR, CH, R, KW, XL, NT, PF>();
+    v.fn[2] = fixed_fn<3, LPR, CH, R, KW, XL, NT, PF>();
+    v.fn[3] = fixed_fn<4, LPR, CH, R, KW, XL, NT, PF>();
     v.k_fixed = KW * LPR * 8 * CH;
     v.rows_per_group = R * (64 / LPR);
     return v;
@@ -65,7 +68,7 @@ template <int U, int R, bool NT>
 Variant loop_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_LOOP_K, 256, 64, U, R, 1, NT ? 1 : 0, 0, 1};
+    v.plan = skinny_plan_t{SKINNY_KIND_LOOP_K, 256, 64, U, R, 1, NT ? 1 : 0, 0, 1, 0};
     v.fn[0] = reinterpret_cast<const void *>(&skg::loop_k_kernel<1, U, R, NT>);
     v.fn[1] = reinterpret_cast<const void *>(&skg::loop_k_kernel<2, U, R, NT>);
     v.fn[2] = reinterpret_cast<const void *>(&skg::loop_k_kernel<3, U, R, NT>);
@@ -78,7 +81,7 @@ Variant loop_variant()
 Variant scalar_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_SCALAR, 256, 64, 1, 1, 1, 0, 0, 0};
+    v.plan = skinny_plan_t{SKINNY_KIND_SCALAR, 256, 64, 1, 1, 1, 0, 0, 0, 0};
     v.fn[0] = reinterpret_cast<const void *>(&skg::scalar_kernel<1>);
     v.fn[1] = reinterpret_cast<const void *>(&skg::scalar_kernel<2>);
     v.fn[2] = reinterpret_cast<const void *>(&skg::scalar_kernel<3>);
@@ -88,18 +91,16 @@ Variant scalar_variant()
     return v;
 }
 
-// Per (lanes_per_row, chunks, k_split): rows per wave 1, 2, 4 with the
-// non-temporal hint and x in registers or LDS, plus the plain-cached form at
-// one row per wave (the hint won every cell of the gfx950 sweep).
-#define SKG_FIXED(LPR, CH, KW)                                                                       \
-    fixed_variant<LPR, CH, 1, KW, false, true>(), fixed_variant<LPR, CH, 2, KW, false, true>(),      \
-        fixed_variant<LPR, CH, 4, KW, false, true>(), fixed_variant<LPR, CH, 1, KW, true, true>(),   \
-        fixed_variant<LPR, CH, 2, KW, true, true>(), fixed_variant<LPR, CH, 4, KW, true, true>(),    \
-        fixed_variant<LPR, CH, 1, KW, false, false>()
-// chunks = 16 leaves room for one or two rows per wave only (see fits())
-#define SKG_FIXED16(LPR, KW)                                                                         \
-    fixed_variant<LPR, 16, 1, KW, false, true>(), fixed_variant<LPR, 16, 1, KW, true, true>(),       \
-        fixed_variant<LPR, 16, 1, KW, false, false>()
+// Per (lanes_per_row, chunks, k_split): one or two rows per wave, x in registers
+// or LDS, with and without tile prefetch, all with the non-temporal hint; plus
+// the plain-cached form at one row per wave (the hint won every cell of the
+// gfx950 sweep).
+#define SKG_FIXED_XP(LPR, CH, KW, XL, PF)                                                          \
+    fixed_variant<LPR, CH, 1, KW, XL, true, PF>(), fixed_variant<LPR, CH, 2, KW, XL, true, PF>()
+#define SKG_FIXED(LPR, CH, KW)                                                                      \
+    SKG_FIXED_XP(LPR, CH, KW, false, false), SKG_FIXED_XP(LPR, CH, KW, false, true),                \
+        SKG_FIXED_XP(LPR, CH, KW, true, false), SKG_FIXED_XP(LPR, CH, KW, true, true),              \
+        fixed_variant<LPR, CH, 1, KW, false, false, true>()
 #define SKG_LOOP(U, R) loop_variant<U, R, false>(), loop_variant<U, R, true>()
 
 // The compiled set. FIXED_K triples (lanes_per_row, chunks, k_split) cover the
@@ -114,7 +115,7 @@ const Variant kAllVariants[] = {
     // K = 4096
     SKG_FIXED(64, 8, 1), SKG_FIXED(64, 4, 2), SKG_FIXED(64, 2, 4),
     // K = 8192
-    SKG_FIXED16(64, 1), SKG_FIXED(64, 8, 2), SKG_FIXED(64, 4, 4),
+    SKG_FIXED(64, 16, 1), SKG_FIXED(64, 8, 2), SKG_FIXED(64, 4, 4),
     // any K % 8 == 0
     SKG_LOOP(2, 1), SKG_LOOP(4, 1), SKG_LOOP(8, 1), SKG_LOOP(2, 2), SKG_LOOP(4, 2),
     // any K, any alignment
@@ -151,7 +152,7 @@ struct PlanEntry {
 };
 const PlanEntry kPlanTable[] = {
 #include "plans_gfx950.inc"
-    {0, 0, 0, {0, 0, 0, 0, 0, 0, 0, 0, 0}},  // sentinel
+    {0, 0, 0, {0, 0, 0, 0, 0, 0, 0, 0, 0, 0}},  // sentinel
 };
 constexpr int kNumPlans = sizeof(kPlanTable) / sizeof(kPlanTable[0]) - 1;
 
@@ -159,7 +160,7 @@ bool same_variant(const skinny_plan_t &a, const skinny_plan_t &b)
 {
     return a.kind == b.kind && a.lanes_per_row == b.lanes_per_row && a.chunks == b.chunks &&
            a.rows_per_wave == b.rows_per_wave && a.k_split == b.k_split &&
-           a.nontemporal == b.nontemporal && a.x_in_lds == b.x_in_lds;
+           a.nontemporal == b.nontemporal && a.x_in_lds == b.x_in_lds && a.prefetch == b.prefetch;
 }
 
 const Variant *find_variant(const skinny_plan_t &p)
@@ -175,7 +176,7 @@ const Variant *find_variant(const skinny_plan_t &p)
 skinny_plan_t default_plan(int N, int K, int M)
 {
     (void)N;
-    skinny_plan_t p{SKINNY_KIND_LOOP_K, 256, 64, 4, 1, 1, 1, 0, 1};
+    skinny_plan_t p{SKINNY_KIND_LOOP_K, 256, 64, 4, 1, 1, 1, 0, 1, 0};
     if (K % 8 != 0)
         return registry().scalar->plan;
     // Prefer a FIXED_K variant for this K with one row per wave, the
@@ -186,7 +187,8 @@ skinny_plan_t default_plan(int N, int K, int M)
     for (int i = 0; i < reg.n; ++i) {
         const Variant &v = *reg.v[i];
         if (v.plan.kind != SKINNY_KIND_FIXED_K || v.k_fixed != K || v.plan.rows_per_wave != 1 ||
-            v.plan.nontemporal != 1 || v.plan.x_in_lds != 0 || v.fn[M - 1] == nullptr)
+            v.plan.nontemporal != 1 || v.plan.x_in_lds != 0 || v.plan.prefetch != 1 ||
+            v.fn[M - 1] == nullptr)
             continue;
         if (!best) {
             best = &v;
@@ -329,6 +331,8 @@ int plan_ok(const skinny_plan_t &p, const Variant *v)
     if (p.kind == SKINNY_KIND_SCALAR && tpb != 256)
         return SKINNY_ERR_INVALID_ARG;
     if (p.x_in_lds != 0 && p.x_in_lds != 1)
+        return SKINNY_ERR_INVALID_ARG;
+    if (p.prefetch != 0 && p.prefetch != 1)
         return SKINNY_ERR_INVALID_ARG;
     return SKINNY_OK;
 }

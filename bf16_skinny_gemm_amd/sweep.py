@@ -2,11 +2,12 @@
 
 For each (N, K, M) it times every compiled variant that can run the shape,
 at several block sizes and with both grid modes (persistent, one block per
-tile), and keeps the fastest. This follows the pages' method (vLLM SM121 plan
-page, section Details: a graph-replay sweep over the plan knobs with the weight
-rotated out of the cache; SM90 plan page: a chain over weight copies of at
-least 1 GiB, captured in a graph, trials of replays), with the copies sized
-past the MI355X's 256 MB Infinity Cache.
+tile), and keeps the fastest. This follows the method of vLLM PR #62949 (SM121
+skinny GEMM plans), section Details (a graph-replay sweep over the plan knobs
+with the weight rotated out of the cache) and vLLM PR #65306 (SM90 skinny GEMM
+plans), section Validation (a graph-captured chain over weight copies of at
+least 1 GiB, timed in trials of replays), with the copies sized past the
+MI355X's 256 MB Infinity Cache.
 
     python -m bf16_skinny_gemm_amd.sweep --out sweep.jsonl          # measure (GPU)
     python -m bf16_skinny_gemm_amd.sweep --emit-inc sweep.jsonl      # write plans_gfx950.inc
@@ -36,7 +37,7 @@ PAIR_SHAPES = [(4096, 128)]
 MS = (1, 2, 3, 4)
 BIG_GRID = 1 << 30  # grid_blocks >= tile count: one block per tile
 PLAN_FIELDS = ("kind", "threads_per_block", "lanes_per_row", "chunks", "rows_per_wave", "k_split",
-               "nontemporal", "grid_blocks", "x_in_lds")
+               "nontemporal", "grid_blocks", "x_in_lds", "prefetch")
 
 
 def log(msg):
@@ -190,7 +191,7 @@ def emit_inc(path, out=INC_PATH):
     lines = [
         "// Tuned launch plans for gfx950, one line per (N, K, M):",
         "//   {N, K, M, {kind, threads_per_block, lanes_per_row, chunks, rows_per_wave, k_split,",
-        "//            nontemporal, grid_blocks, x_in_lds}},",
+        "//            nontemporal, grid_blocks, x_in_lds, prefetch}},",
         "// Generated by `python -m bf16_skinny_gemm_amd.sweep --emit-inc` from an on-device sweep",
         "// (MI355X, weights rotated over >= 1 GiB of copies, hipGraph replay). Do not edit by hand.",
     ]

@@ -7,14 +7,13 @@
  *     y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),   m < M, n < N, k < K,
  *
  * with float32 accumulation and one round-to-nearest-even step to bfloat16 at
- * the end. It is the skinny GEMM of the vLLM pull requests "GLM-5.3-Flash
- * skinny GEMM plans for SM121" (Overview and Claims: BF16 attention, shared-
- * expert and LM-head projections at M = 1/2/4, compared against F.linear in
- * section Validation) and "SM90 skinny GEMM plans" (Overview: 1..4 tokens;
- * Details: one launch per GEMM, no separate reduce kernel). The paired entry
- * point is the batched f_b_proj / g_b_proj projection of the vLLM pull request
- * "Batch paired KDA gate projections" (section "Purpose and source": two
- * same-shape BF16 projections in one batched call).
+ * the end. It is the skinny GEMM of vLLM PR #62949 (SM121 skinny GEMM plans;
+ * Overview and Claims: BF16 attention, shared-expert and LM-head projections at
+ * M = 1/2/4, checked against F.linear in section Validation) and vLLM PR #65306
+ * (SM90 skinny GEMM plans; Overview: 1..4 tokens; Details: one launch per GEMM,
+ * no separate reduce kernel). The paired entry point is the batched f_b_proj /
+ * g_b_proj projection of vLLM PR #57617 (paired KDA gate projections; section
+ * "Purpose and source": two same-shape BF16 projections in one batched call).
  *
  * Conventions shared by every entry point below:
  *  - Pointers x, W, y are DEVICE pointers to bfloat16 values stored as raw
@@ -67,15 +66,15 @@ typedef enum skinny_status {
 /* Kernel families a plan can name. */
 typedef enum skinny_kind {
     SKINNY_KIND_FIXED_K = 1, /* K fixed at compile time = k_split*lanes_per_row*8*chunks;
-                                x in registers or LDS, tiles software-pipelined */
+                                x in registers or LDS, tiles optionally software-pipelined */
     SKINNY_KIND_LOOP_K = 2,  /* any K % 8 == 0; x staged in LDS; chunks = loads in flight per row */
     SKINNY_KIND_SCALAR = 3   /* any K, any alignment; element-wise loads */
 } skinny_kind_t;
 
-/* One launch configuration ("plan"): the knobs of the pages' plan tuple
- * (block size, outputs per block, K unroll, vector width, static K; vLLM SM121
- * plan page, section Details) recast for 64-wide wavefronts. Vector width is
- * fixed at 8 bfloat16 (one 128-bit load per lane). */
+/* One launch configuration ("plan"): the knobs of the plan tuple of vLLM PR
+ * #62949 (SM121 skinny GEMM plans), section Details -- block size, outputs per
+ * block, K unroll, vector width, static K -- recast for 64-wide wavefronts.
+ * Vector width is fixed at 8 bfloat16 (one 128-bit load per lane). */
 typedef struct skinny_plan {
     int32_t kind;              /* skinny_kind_t */
     int32_t threads_per_block; /* 64 * waves per block */
@@ -94,6 +93,9 @@ typedef struct skinny_plan {
     int32_t x_in_lds;          /* FIXED_K: 1 = x staged once per block in LDS, 0 = each lane
                                   keeps its slice of x in registers; LOOP_K: always 1;
                                   SCALAR: always 0 */
+    int32_t prefetch;          /* FIXED_K: 1 = the next tile's weights are loaded while the
+                                  current tile is consumed (two register sets); 0 = one tile
+                                  at a time; other kinds: always 0 */
 } skinny_plan_t;
 
 /* Checks that `device` is a gfx950 GPU and caches its properties. Optional:
@@ -104,16 +106,17 @@ int skinny_gemm_init(int device);
 
 /* y = x . W^T with the plan the library's table holds for (N, K, M) on this
  * architecture, or its default plan when the table has no entry. The table is
- * keyed like the pages' plan tables: architecture + local (N, K) + M (vLLM SM90
- * plan page, section Details). */
+ * keyed like the plan tables of vLLM PR #65306 (SM90 skinny GEMM plans),
+ * section Details: architecture + local (N, K) + M. */
 int skinny_gemm_bf16(const void *x, const void *W, void *y,
                      int M, int N, int K, hipStream_t stream);
 
 /* The paired projection: y0 = x . W0^T and y1 = x . W1^T, both [N][K] weights
- * applied to the one shared x, in ONE kernel launch (vLLM "Batch paired KDA
- * gate projections", section "Purpose and source"; the batched f_b/g_b row of
- * the LMDeploy GLM-5.3 page's operator-level gains table). Same conventions as
- * skinny_gemm_bf16; y0 and y1 must not overlap each other, x, W0 or W1. */
+ * applied to the one shared x, in ONE kernel launch (vLLM PR #57617, paired KDA
+ * gate projections, section "Purpose and source"; LMDeploy PR #4968, GLM-5.3
+ * Flash support, the batched f_b/g_b row of its operator-level gains table).
+ * Same conventions as skinny_gemm_bf16; y0 and y1 must not overlap each other,
+ * x, W0 or W1. */
 int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1,
                           void *y0, void *y1, int M, int N, int K, hipStream_t stream);
 

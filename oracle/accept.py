@@ -5,11 +5,11 @@ G1 (per element, gate):   |y - y_ref| <= 1e-2 * mag + 1e-6,
 G2 (per output row, gate): cosine(y[m, :], y_ref[m, :]) >= 0.99999 in float64;
     two all-zero rows agree, exactly one all-zero row disagrees.
 S1 (per element, strict):  |y - ref64| <= 7.5e-5 + 2**-8 * |ref64|, the float64
-    comparison rule of the vLLM SM90 skinny-GEMM plan page (section "How it was
-    measured").
+    comparison rule of vLLM PR #65306 (SM90 skinny GEMM plans), section
+    Validation.
 
-G1 and G2 are the bar the HIP path must meet; S1 is the pages' own, tighter
-rule and the parity tests assert it as well.
+G1 and G2 are the bar the HIP path must meet; S1 is the cited pull request's
+own, tighter rule, and the parity tests assert it as well.
 """
 from __future__ import annotations
 

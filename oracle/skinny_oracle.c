@@ -13,13 +13,14 @@
  *   y[m,n]     = bf16_rne(ref64[m,n])                               (one rounding)
  *
  * Sources: the operation is F.linear on bfloat16 tensors at 1..4 tokens (vLLM
- * PR "GLM-5.3-Flash skinny GEMM plans for SM121", section Validation: outputs
- * compared with F.linear); the reference precision is float64 (vLLM PR "SM90
- * skinny GEMM plans", section "How it was measured": elementwise comparison with
- * a float64 reference). Each product of two bfloat16 values is exact in double
- * (8 + 8 significant bits), so only the sums round, at double precision.
+ * PR #62949, SM121 skinny GEMM plans, section Validation: outputs compared with
+ * F.linear); the reference precision is float64 (vLLM PR #65306, SM90 skinny
+ * GEMM plans, section Validation: elementwise comparison with a float64
+ * reference). Each product of two bfloat16 values is exact in double (8 + 8
+ * significant bits), so only the sums round, at double precision.
  *
- * Rounding to bfloat16 (the reading taken where the pages are silent):
+ * Rounding to bfloat16 (the reading taken where the cited pull requests are
+ * silent):
  * IEEE-754 round-to-nearest, ties-to-even, applied once, directly from the
  * double value (no intermediate float rounding); results beyond the largest
  * finite bfloat16 by half an ulp or more become +-Inf; NaN becomes a quiet NaN

@@ -7,15 +7,15 @@ own float32 -> bfloat16 conversion (round to nearest even), then handed out as
 raw uint16 bit patterns. Nothing here multiplies, accumulates or rounds an
 output.
 
-Workload recipe (the decode projections of the vLLM skinny-GEMM plan pages,
-"Validation" tables): activations x ~ N(0, 1), weights W ~ N(0, 1/K), i.e.
+Workload recipe (the decode projections of vLLM PR #62949, SM121 skinny GEMM
+plans, section Validation): activations x ~ N(0, 1), weights W ~ N(0, 1/K), i.e.
 standard deviation 1/sqrt(K), row-major, seed 0, one independent stream per
 tensor derived as ``default_rng([seed, shape_id, tensor_id])``.
 
-Robustness classes named by the SM90 plan page ("How it was measured": normal,
-outlier and scaled/sparse inputs) are left undefined there; the reading used
-here is: outlier = 1% of x's K channels multiplied by 64, scaled = x times
-2**s, sparse = 90% of x's entries set to zero.
+vLLM PR #65306 (SM90 skinny GEMM plans), section Validation, also checks
+outlier and scaled/sparse inputs without defining them; the reading used here
+is: outlier = 1% of x's K channels multiplied by 64, scaled = x times 2**s,
+sparse = 90% of x's entries set to zero.
 """
 from __future__ import annotations
 

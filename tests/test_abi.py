@@ -125,7 +125,7 @@ def test_plan_table_entries_are_valid(skg):
     rows = re.findall(r"^\s*\{\s*(\d+),\s*(\d+),\s*(\d+),\s*\{([^}]*)\}\s*\},", open(inc).read(), re.M)
     keys = set()
     vset = {tuple(v.as_dict()[k] for k in ("kind", "lanes_per_row", "chunks", "rows_per_wave",
-                                           "k_split", "nontemporal", "x_in_lds"))
+                                           "k_split", "nontemporal", "x_in_lds", "prefetch"))
             for v in skg.variants()}
     for N, K, M, fields in rows:
         N, K, M = int(N), int(K), int(M)
@@ -135,9 +135,9 @@ def test_plan_table_entries_are_valid(skg):
         assert tuned
         vals = [int(v) for v in fields.split(",")]
         assert vals == [p.kind, p.threads_per_block, p.lanes_per_row, p.chunks, p.rows_per_wave,
-                        p.k_split, p.nontemporal, p.grid_blocks, p.x_in_lds]
+                        p.k_split, p.nontemporal, p.grid_blocks, p.x_in_lds, p.prefetch]
         assert (p.kind, p.lanes_per_row, p.chunks, p.rows_per_wave, p.k_split, p.nontemporal,
-                p.x_in_lds) in vset
+                p.x_in_lds, p.prefetch) in vset
         if p.kind == skg.SKINNY_KIND_FIXED_K:
             assert _fixed_k(p) == K
         assert 1 <= M <= 4 and p.threads_per_block // 64 % p.k_split == 0
@@ -214,18 +214,18 @@ def test_ex_rejects_bad_plans(skg):
         skg.SKINNY_ERR_UNSUPPORTED
     # compiled variant, wrong K for a fixed-K plan
     p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
-             k_split=1, nontemporal=0, grid_blocks=0)
+             k_split=1, nontemporal=1, grid_blocks=0, prefetch=1)
     assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 2048, ctypes.byref(p), None) == \
         skg.SKINNY_ERR_INVALID_ARG
     # x_in_lds must be 0 or 1
     p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
-             k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=2)
+             k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=2, prefetch=1)
     assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) in \
         (skg.SKINNY_ERR_INVALID_ARG, skg.SKINNY_ERR_UNSUPPORTED)
     # block size not a multiple of 64 * k_split, too large, negative grid
     for tpb, ks, ch, grid in ((96, 1, 2, 0), (1024, 1, 2, 0), (64, 2, 1, 0), (256, 1, 2, -1)):
         p = Plan(kind=1, threads_per_block=tpb, lanes_per_row=64, chunks=ch, rows_per_wave=1,
-                 k_split=ks, nontemporal=0, grid_blocks=grid)
+                 k_split=ks, nontemporal=1, grid_blocks=grid, prefetch=1)
         assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) == \
             skg.SKINNY_ERR_INVALID_ARG, (tpb, ks, grid)
     # a vector plan on a misaligned pointer or K % 8 != 0 is an error, not a silent fallback

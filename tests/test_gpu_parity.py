@@ -1,12 +1,12 @@
 """Parity of the HIP path with the CPU oracle on an MI355X (gfx950).
 
 Every call goes through the C ABI (the ctypes binding passes raw device
-pointers and torch's current stream). The bar, from the task's definition of
-the method: per element |y - y_ref| <= 1e-2 * sum_k |x_k W_nk| + 1e-6, per
-output row cosine >= 0.99999, and additionally the float64 rule of the SM90
-plan page, |y - ref64| <= 7.5e-5 + 2^-8 |ref64| (oracle/accept.py). Exact
-cases (zero, identity, one-hot, small integers, rounding ties) must match bit
-for bit.
+pointers and torch's current stream). The acceptance bar: per element
+|y - y_ref| <= 1e-2 * sum_k |x_k W_nk| + 1e-6, per output row cosine >= 0.99999,
+and additionally the float64 rule of vLLM PR #65306 (SM90 skinny GEMM plans),
+section Validation: |y - ref64| <= 7.5e-5 + 2^-8 |ref64|
+(oracle/accept.py). Exact cases (zero, identity, one-hot, small integers,
+rounding ties) must match bit for bit.
 """
 from __future__ import annotations
 
@@ -83,7 +83,7 @@ def _variant_cases():
     except Exception:  # library missing: collected as one failing case
         return [pytest.param(None, id="no-library")]
     return [pytest.param(v, id=f"v{i}-k{v.kind}-l{v.lanes_per_row}-c{v.chunks}-r{v.rows_per_wave}"
-                                f"-s{v.k_split}-nt{v.nontemporal}-x{v.x_in_lds}")
+                                f"-s{v.k_split}-nt{v.nontemporal}-x{v.x_in_lds}-p{v.prefetch}")
             for i, v in enumerate(vs)]
 
 
@@ -419,7 +419,8 @@ def test_rejects_m5(skg):
 
 @pytest.mark.parametrize("kind", ["outlier", "scaled_up", "scaled_down", "sparse"])
 def test_robustness_inputs(skg, kind):
-    """The SM90 page's input classes beyond normal: outlier, scaled and sparse."""
+    """Input classes beyond normal (vLLM PR #65306, section Validation): outlier,
+    scaled and sparse."""
     for (N, K) in [(4096, 1024), (2048, 4096), (8192, 1536)]:
         for M in (1, 4):
             if kind == "outlier":
