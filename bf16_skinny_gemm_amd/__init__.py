@@ -36,6 +36,7 @@ SKINNY_ERR_LAUNCH = -4
 SKINNY_KIND_FIXED_K = 1
 SKINNY_KIND_LOOP_K = 2
 SKINNY_KIND_SCALAR = 3
+SKINNY_KIND_MFMA = 4
 
 
 class SkinnyError(RuntimeError):
@@ -260,4 +261,5 @@ __all__ = [
     "skinny_gemm_get_variant", "skinny_gemm_status_string", "skinny_gemm_version",
     "SKINNY_OK", "SKINNY_ERR_INVALID_ARG", "SKINNY_ERR_UNSUPPORTED", "SKINNY_ERR_NOT_INITIALIZED",
     "SKINNY_ERR_LAUNCH", "SKINNY_KIND_FIXED_K", "SKINNY_KIND_LOOP_K", "SKINNY_KIND_SCALAR",
+    "SKINNY_KIND_MFMA",
 ]

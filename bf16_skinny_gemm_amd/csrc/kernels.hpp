@@ -53,6 +53,40 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, unsigned byte_
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_offset, 0, NT ? kAuxNontemporal : 0);
 }
 
+// Staging of x into LDS, split so that it overlaps the first weight loads:
+// stage_issue() loads the first kStageBatch 16-byte pieces per thread (call it
+// before issuing weights), stage_finish() writes them to LDS once they arrive
+// and copies any rest. Only the waits for these x loads stand between the
+// kernel start and the barrier, not one round trip per loop iteration.
+// `src(i)` gives the byte offset of piece i in x, or kOutOfRange for zeros.
+constexpr int kStageBatch = 8;
+
+template <typename Src>
+__device__ __forceinline__ void stage_issue(__amdgpu_buffer_rsrc_t xs, int npieces, Src src,
+                                            u32x4 (&t)[kStageBatch])
+{
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+        const int i = (int)threadIdx.x + u * (int)blockDim.x;
+        t[u] = load16<false>(xs, i < npieces ? src(i) : kOutOfRange);
+    }
+}
+
+template <typename Src>
+__device__ __forceinline__ void stage_finish(__amdgpu_buffer_rsrc_t xs, int npieces, Src src,
+                                             const u32x4 (&t)[kStageBatch], u32x4 *dst)
+{
+#pragma unroll
+    for (int u = 0; u < kStageBatch; ++u) {
+        const int i = (int)threadIdx.x + u * (int)blockDim.x;
+        if (i < npieces)
+            dst[i] = t[u];
+    }
+    for (int i = (int)threadIdx.x + kStageBatch * (int)blockDim.x; i < npieces; i += (int)blockDim.x)
+        dst[i] = load16<false>(xs, src(i));
+    __syncthreads();
+}
+
 // acc + w.lo*x.lo + w.hi*x.hi, the two bfloat16 products exact, float32 sum.
 __device__ __forceinline__ float dot2(unsigned w, unsigned x, float acc)
 {
@@ -213,25 +247,25 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     if (tile >= a.total_tiles)
         return;  // whole block
 
-    u32x4 wa[R][CH], wb[PF ? R : 1][PF ? CH : 1];
-    F::issue(a, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
-
     __shared__ u32x4 x_lds[XL ? M * K / 8 : 1];
     __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
+    u32x4 wa[R][CH], wb[PF ? R : 1][PF ? CH : 1];
     u32x4 xr[XL ? 1 : M][XL ? 1 : CH];
-    {
-        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
-        if constexpr (XL) {
-            for (int i = threadIdx.x; i < M * K / 8; i += (int)blockDim.x)
-                x_lds[i] = load16<false>(xs, (unsigned)i * 16u);
-            __syncthreads();
-        } else {
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+    if constexpr (XL) {
+        // x pieces first (L2), then the weights (HBM), then x into LDS
+        auto src = [](int i) { return (unsigned)i * 16u; };
+        u32x4 xt[kStageBatch];
+        stage_issue(xs, M * K / 8, src, xt);
+        F::issue(a, tile, rows_t, grp, sub, kbase, wa);
+        stage_finish(xs, M * K / 8, src, xt, x_lds);
+    } else {
+        F::issue(a, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
 #pragma unroll
-            for (int m = 0; m < M; ++m)
+        for (int m = 0; m < M; ++m)
 #pragma unroll
-                for (int j = 0; j < CH; ++j)
-                    xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
-        }
+            for (int j = 0; j < CH; ++j)
+                xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
     }
 
     auto consume = [&](int t, const u32x4 (&wv)[R][CH]) {
@@ -352,13 +386,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
 
     {
         const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
-        for (int i = threadIdx.x; i < M * kvec; i += (int)blockDim.x) {
+        auto src = [=](int i) {
             const int m = i / kvec;
             const int kv = i - m * kvec;
-            const unsigned off = kv * 8 < K ? (unsigned)(m * K + kv * 8) * 2u : kOutOfRange;
-            lds_x[i] = load16<false>(xs, off);
-        }
-        __syncthreads();
+            return kv * 8 < K ? (unsigned)(m * K + kv * 8) * 2u : kOutOfRange;
+        };
+        u32x4 xt[kStageBatch];
+        stage_issue(xs, M * kvec, src, xt);
+        stage_finish(xs, M * kvec, src, xt, lds_x);
     }
 
     const int rows_t = (int)(blockDim.x >> 6) * R;
@@ -418,6 +453,214 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
                         ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m][r]);
                 }
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Family MFMA: the matrix cores do the multiplies.
+//
+// v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products per wave: block
+// b = lanes 4b .. 4b+3, and lane (b, j) supplies row j of the block's A (4
+// bfloat16), column j of its B, and holds column j of its 4x4 float32
+// accumulator (one VGPR per row). Here A = x (row m, zero-cost padding for
+// m >= M) and B = W^T (column j = output row j of a 4-row group), and the 16
+// blocks take 16 consecutive 8-element K chunks of the same 4 rows. So lane
+// (b, j) loads 16 bytes W[row j][k0 + 8b .. +8], which feed two MFMAs (k 0..3,
+// then 4..7), and one load instruction reads 4 rows x 256 contiguous bytes.
+// The A operand is x[m = j][the same 8 k], one 16-byte LDS read. Lanes j >= M
+// read a valid x row: they only feed rows m >= M of the result, never stored.
+// After the K loop the 16 block partials of each (m, row) are summed across
+// lanes (DPP row rotations, then two cross-row shuffles), once per tile.
+//
+// A wave owns R groups of 4 rows; KW waves of a block split K and meet in LDS
+// (fixed order). The K loop runs in batches of U loads per group; with PF the
+// next batch (or the next tile's first batch) is loaded while the current one
+// is multiplied. Requires K % (128 * KW) == 0 and (K / KW / 128) % U == 0.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma4x4x4(unsigned a0, unsigned a1, unsigned b0, unsigned b1,
+                                             f32x4_t c)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s16x4_t, u32x2{a0, a1}),
+                                                  __builtin_bit_cast(s16x4_t, u32x2{b0, b1}), c,
+                                                  0, 0, 0);
+}
+
+template <int M, int U, int R, int KW, bool NT, bool PF>
+__global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
+{
+    extern __shared__ u32x4 mx_lds[];  // x as [M][K] bfloat16
+    constexpr int ROWS_W = 4 * R;
+    __shared__ float part[KW > 1 ? kMaxWaves * ROWS_W * M : 1];
+
+    const int K = a.K;
+    const int kslice = K / KW;
+    const int nb = kslice / (128 * U);  // batches per tile
+    const int groups = (int)(blockDim.x >> 6) / KW;
+    const int rows_t = groups * ROWS_W;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kw = wave % KW;
+    const int grp = wave / KW;
+    const int lj = lane & 3;   // row of A / column of B and D within a block
+    const int lb = lane >> 2;  // block: which 8-element K chunk
+    const int xrow = lj < M ? lj : 0;
+    const int step = (int)gridDim.x;
+
+    int tile = blockIdx.x;
+    if (tile >= a.total_tiles)
+        return;  // whole block
+
+    // W loads of batch b of tile t for this wave's R groups.
+    auto issue = [&](int t, int b, u32x4 (&wv)[R][U]) {
+        const uint16_t *base = a.w0;
+        int valid = 0;
+        if (t < a.total_tiles) {
+            const int mat = t >= a.tiles_per_mat ? 1 : 0;
+            const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+            valid = a.N - row0;
+            valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
+            base = (mat ? a.w1 : a.w0) + (size_t)row0 * K;
+        }
+        const __amdgpu_buffer_rsrc_t ws = make_rsrc(base, (unsigned)(valid * K * 2));
+        const unsigned k0 = (unsigned)(kw * kslice + b * 128 * U + lb * 8);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                wv[r][u] = load16<NT>(ws, ((unsigned)((r * 4 + lj) * K) + k0 + u * 128) * 2u);
+    };
+
+    u32x4 wa[R][U], wb[PF ? R : 1][PF ? U : 1];
+    {
+        // x pieces first (L2), then the weights (HBM), then x into LDS
+        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+        auto src = [](int i) { return (unsigned)i * 16u; };
+        u32x4 xt[kStageBatch];
+        stage_issue(xs, M * K / 8, src, xt);
+        issue(tile, 0, wa);
+        stage_finish(xs, M * K / 8, src, xt, mx_lds);
+    }
+
+    f32x4_t acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto multiply = [&](int b, const u32x4 (&wv)[R][U]) {
+        const int xk = kw * kslice + b * 128 * U + lb * 8;
+        const volatile __attribute__((address_space(3))) u32x4 *xp =
+            (const volatile __attribute__((address_space(3))) u32x4 *)mx_lds;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 xv = xp[(xrow * K + xk + u * 128) / 8];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                acc[r] = mfma4x4x4(xv[0], xv[1], wv[r][u][0], wv[r][u][1], acc[r]);
+                acc[r] = mfma4x4x4(xv[2], xv[3], wv[r][u][2], wv[r][u][3], acc[r]);
+            }
+        }
+    };
+
+    // Sum the 16 block partials: lanes j, j+4, ..., j+60 hold the same (m, row).
+    auto block_sum = [&](float v) {
+        v = dpp_add<0x124>(v);  // row_ror:4
+        v = dpp_add<0x128>(v);  // row_ror:8
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        return v;
+    };
+
+    auto finish = [&](int t) {
+        const int mat = t >= a.tiles_per_mat ? 1 : 0;
+        uint16_t *ym = mat ? a.y1 : a.y0;
+        const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+        float s[R][M];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                s[r][m] = block_sum(acc[r][m]);
+        if constexpr (KW == 1) {
+            if (lb == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int row = row0 + r * 4 + lj;
+                    if (row < a.N) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m)
+                            ym[(size_t)m * a.N + row] = f32_to_bf16(s[r][m]);
+                    }
+                }
+            }
+        } else {
+            if (lb == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < M; ++m)
+                        part[((grp * KW + kw) * ROWS_W + r * 4 + lj) * M + m] = s[r][m];
+            }
+            __syncthreads();
+            if (kw == 0 && lb == 0) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int rr = r * 4 + lj;
+                    const int row = row0 + rr;
+                    if (row < a.N) {
+#pragma unroll
+                        for (int m = 0; m < M; ++m) {
+                            float v = part[((grp * KW + 0) * ROWS_W + rr) * M + m];
+#pragma unroll
+                            for (int q = 1; q < KW; ++q)
+                                v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
+                            ym[(size_t)m * a.N + row] = f32_to_bf16(v);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    int b = 0;
+    if constexpr (PF) {
+        // One step: load the next batch into `nxt`, multiply `cur`, close the tile
+        // after its last batch. Returns false when no step follows.
+        auto run_step = [&](const u32x4 (&cur)[R][U], u32x4 (&nxt)[R][U]) {
+            int t2 = tile, b2 = b + 1;
+            if (b2 == nb) {
+                b2 = 0;
+                t2 = tile + step;
+            }
+            issue(t2, b2, nxt);
+            multiply(b, cur);
+            if (b + 1 == nb)
+                finish(tile);
+            tile = t2;
+            b = b2;
+            return tile < a.total_tiles;
+        };
+        while (run_step(wa, wb) && run_step(wb, wa)) {
+        }
+    } else {
+        while (true) {
+            multiply(b, wa);
+            if (++b == nb) {
+                finish(tile);
+                b = 0;
+                tile += step;
+                if (tile >= a.total_tiles)
+                    break;
+            }
+            issue(tile, b, wa);
         }
     }
 }

@@ -78,6 +78,21 @@ Variant loop_variant()
     return v;
 }
 
+template <int U, int R, int KW, bool PF>
+Variant mfma_variant()
+{
+    Variant v{};
+    const int tpb = 64 * (KW > 4 ? KW : 4);
+    v.plan = skinny_plan_t{SKINNY_KIND_MFMA, tpb, 16, U, R, KW, 1, 0, 1, PF ? 1 : 0};
+    v.fn[0] = reinterpret_cast<const void *>(&skg::mfma_kernel<1, U, R, KW, true, PF>);
+    v.fn[1] = reinterpret_cast<const void *>(&skg::mfma_kernel<2, U, R, KW, true, PF>);
+    v.fn[2] = reinterpret_cast<const void *>(&skg::mfma_kernel<3, U, R, KW, true, PF>);
+    v.fn[3] = reinterpret_cast<const void *>(&skg::mfma_kernel<4, U, R, KW, true, PF>);
+    v.k_fixed = 0;
+    v.rows_per_group = 4 * R;
+    return v;
+}
+
 Variant scalar_variant()
 {
     Variant v{};
@@ -102,6 +117,8 @@ Variant scalar_variant()
         SKG_FIXED_XP(LPR, CH, KW, true, false), SKG_FIXED_XP(LPR, CH, KW, true, true),              \
         fixed_variant<LPR, CH, 1, KW, false, false, true>()
 #define SKG_LOOP(U, R) loop_variant<U, R, false>(), loop_variant<U, R, true>()
+#define SKG_MFMA_PF(U, R, KW) mfma_variant<U, R, KW, false>(), mfma_variant<U, R, KW, true>()
+#define SKG_MFMA(U, R) SKG_MFMA_PF(U, R, 1), SKG_MFMA_PF(U, R, 2), SKG_MFMA_PF(U, R, 4), SKG_MFMA_PF(U, R, 8)
 
 // The compiled set. FIXED_K triples (lanes_per_row, chunks, k_split) cover the
 // K of the decode projections: 128 (paired f_b/g_b), 1024, 1536, 4096, 8192.
@@ -118,6 +135,8 @@ const Variant kAllVariants[] = {
     SKG_FIXED(64, 16, 1), SKG_FIXED(64, 8, 2), SKG_FIXED(64, 4, 4),
     // any K % 8 == 0
     SKG_LOOP(2, 1), SKG_LOOP(4, 1), SKG_LOOP(8, 1), SKG_LOOP(2, 2), SKG_LOOP(4, 2),
+    // matrix cores: K % (128 * k_split * chunks) == 0
+    SKG_MFMA(1, 1), SKG_MFMA(2, 1), SKG_MFMA(4, 1), SKG_MFMA(8, 1), SKG_MFMA(2, 2), SKG_MFMA(4, 2),
     // any K, any alignment
     scalar_variant(),
 };
@@ -238,11 +257,15 @@ int check_device(int dev, DevInfo *out)
     DevInfo &d = g_dev[dev];
     if (d.state == 0) {
         int count = 0;
-        if (hipGetDeviceCount(&count) != hipSuccess || dev >= count)
+        if (hipGetDeviceCount(&count) != hipSuccess || dev >= count) {
+            (void)hipGetLastError();
             return SKINNY_ERR_INVALID_ARG;
+        }
         hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
             return SKINNY_ERR_UNSUPPORTED;
+        }
         if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
             d.state = SKINNY_ERR_UNSUPPORTED;
         } else {
@@ -263,8 +286,10 @@ int check_device(int dev, DevInfo *out)
 int current_device(DevInfo *out)
 {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess)
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
         return SKINNY_ERR_UNSUPPORTED;
+    }
     return check_device(dev, out);
 }
 
@@ -319,6 +344,13 @@ bool vector_ok(const Call &c)
     return al && c.K % 8 == 0 && c.K <= (1 << 20);
 }
 
+// The MFMA family needs whole batches of 128 * chunks in every k_split slice.
+bool mfma_k_ok(const skinny_plan_t &p, int K)
+{
+    const int per = 128 * p.k_split;
+    return K % per == 0 && (K / per) % p.chunks == 0;
+}
+
 int plan_ok(const skinny_plan_t &p, const Variant *v)
 {
     if (!v)
@@ -337,26 +369,59 @@ int plan_ok(const skinny_plan_t &p, const Variant *v)
     return SKINNY_OK;
 }
 
+// Launch and, on failure, clear the runtime's sticky last-error so that a refused
+// launch is reported once, here, and not again by the caller's next HIP call.
 hipError_t launch(const void *fn, int grid, int block, size_t lds, void **args, hipStream_t s)
 {
-    return hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, lds, s);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, lds, s);
+    if (e != hipSuccess)
+        (void)hipGetLastError();
+    return e;
 }
 
 std::atomic<int> g_lds_raised[kNumAll][4];
-std::atomic<int> g_occupancy[kNumAll][4][skg::kMaxWaves + 1];
+std::atomic<int> g_static_lds[kNumAll][4];  // static LDS bytes + 1 (0 = not queried)
 
-// Blocks of this kernel one CU holds at once (cached; 1 if the query fails).
+// Static LDS of a kernel (its __shared__ arrays), queried once.
+int static_lds(int vidx, int M, const void *fn)
+{
+    std::atomic<int> &slot = g_static_lds[vidx][M - 1];
+    int v = slot.load(std::memory_order_acquire);
+    if (v > 0)
+        return v - 1;
+    hipFuncAttributes attr{};
+    if (hipFuncGetAttributes(&attr, fn) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    slot.store((int)attr.sharedSizeBytes + 1, std::memory_order_release);
+    return (int)attr.sharedSizeBytes;
+}
+
+// Blocks of this kernel one CU holds at once (cached per kernel, block size
+// and LDS size; 1 if the query fails).
+struct OccEntry {
+    int vidx, M, tpb;
+    size_t lds;
+    int blocks;
+};
+std::mutex g_occ_mu;
+OccEntry g_occ[512];
+int g_occ_n = 0;
+
 int blocks_per_cu(int vidx, int M, const void *fn, int tpb, size_t lds)
 {
-    std::atomic<int> &slot = g_occupancy[vidx][M - 1][tpb / 64];
-    int n = slot.load(std::memory_order_acquire);
-    if (n > 0)
-        return n;
-    n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, tpb, lds) != hipSuccess || n < 1)
+    std::lock_guard<std::mutex> lk(g_occ_mu);
+    for (int i = 0; i < g_occ_n; ++i)
+        if (g_occ[i].vidx == vidx && g_occ[i].M == M && g_occ[i].tpb == tpb && g_occ[i].lds == lds)
+            return g_occ[i].blocks;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, tpb, lds) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
         n = 1;
-    if (lds == 0)
-        slot.store(n, std::memory_order_release);
+    }
+    if (g_occ_n < (int)(sizeof(g_occ) / sizeof(g_occ[0])))
+        g_occ[g_occ_n++] = OccEntry{vidx, M, tpb, lds, n};
     return n;
 }
 
@@ -375,6 +440,8 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         if (c.M > 0 && v->fn[c.M - 1] == nullptr)
             return SKINNY_ERR_UNSUPPORTED;
         if (c.M > 0 && c.N > 0 && c.K > 0 && v->plan.kind != SKINNY_KIND_SCALAR && !vector_ok(c))
+            return SKINNY_ERR_INVALID_ARG;
+        if (c.K > 0 && v->plan.kind == SKINNY_KIND_MFMA && !mfma_k_ok(v->plan, c.K))
             return SKINNY_ERR_INVALID_ARG;
     }
     if (c.M == 0 || c.N == 0)
@@ -416,6 +483,8 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         if (!v || v->k_fixed != c.K || !v->fn[c.M - 1])
             plan = default_plan(c.N, c.K, c.M);
     }
+    if (!plan_in && plan.kind == SKINNY_KIND_MFMA && !mfma_k_ok(plan, c.K))
+        plan = default_plan(c.N, c.K, c.M);
     const Variant *v = find_variant(plan);
     if (!v || plan_ok(plan, v) != SKINNY_OK || !v->fn[c.M - 1])
         return SKINNY_ERR_UNSUPPORTED;
@@ -456,48 +525,54 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         int grid = (int)total;
         if (plan.grid_blocks > 0 && plan.grid_blocks < grid)
             grid = plan.grid_blocks;
-        if (plan.kind == SKINNY_KIND_FIXED_K) {
-            // Default: a persistent grid that fills the device once, so every wave
-            // loads its x slice once and then streams many rows.
-            if (plan.grid_blocks == 0) {
-                const long long cap =
-                    (long long)dev.cus * blocks_per_cu(vidx, c.M, v->fn[c.M - 1], plan.threads_per_block, 0);
-                if (cap < grid)
-                    grid = (int)cap;
+        // Dynamic LDS: x staged as [M][Kpad] (LOOP_K) or [M][K] (MFMA).
+        int kpad = c.K;
+        size_t lds = 0;
+        if (plan.kind == SKINNY_KIND_LOOP_K) {
+            const int kstep = 512 * plan.chunks;
+            kpad = ((c.K + kstep - 1) / kstep) * kstep;
+            lds = (size_t)c.M * kpad * 2;
+        } else if (plan.kind == SKINNY_KIND_MFMA) {
+            lds = (size_t)c.M * c.K * 2;
+        }
+        const void *fn = v->fn[c.M - 1];
+        int block = plan.threads_per_block;
+        const int st_lds = lds > 0 ? static_lds(vidx, c.M, fn) : 0;
+        if (st_lds < 0)
+            return SKINNY_ERR_LAUNCH;
+        if (lds + (size_t)st_lds > (size_t)dev.max_lds) {
+            if (plan_in)
+                return SKINNY_ERR_UNSUPPORTED;
+            // x does not fit in LDS: element-wise path
+            fn = registry().scalar->fn[c.M - 1];
+            const long long blocks = ((long long)c.nmats * c.N + 3) / 4;
+            int nmats = c.nmats;
+            void *args[] = {&a, &nmats};
+            err = launch(fn, (int)blocks, 256, 0, args, stream);
+            return err == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
+        }
+        if (lds > 65536 && !g_lds_raised[vidx][c.M - 1].load(std::memory_order_acquire)) {
+            // allow this kernel the whole LDS of a block beside its static arrays
+            if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    dev.max_lds - st_lds) != hipSuccess) {
+                (void)hipGetLastError();
+                return SKINNY_ERR_LAUNCH;
             }
-            void *args[] = {&a};
-            err = launch(v->fn[c.M - 1], grid, plan.threads_per_block, 0, args, stream);
+            g_lds_raised[vidx][c.M - 1].store(1, std::memory_order_release);
+        }
+        // Default: a persistent grid that fills the device once, so every wave
+        // loads x once and then streams many rows.
+        if (plan.grid_blocks == 0) {
+            const long long cap = (long long)dev.cus * blocks_per_cu(vidx, c.M, fn, block, lds);
+            if (cap < grid)
+                grid = (int)cap;
+        }
+        if (plan.kind == SKINNY_KIND_LOOP_K) {
+            void *args[] = {&a, &kpad};
+            err = launch(fn, grid, block, lds, args, stream);
         } else {
-            const int step = 512 * plan.chunks;
-            int kpad = ((c.K + step - 1) / step) * step;
-            const size_t lds = (size_t)c.M * kpad * 2;
-            if (lds > (size_t)dev.max_lds) {
-                if (plan_in)
-                    return SKINNY_ERR_UNSUPPORTED;
-                // x does not fit in LDS: element-wise path
-                const Variant *sv = registry().scalar;
-                int nmats = c.nmats;
-                const long long blocks = ((long long)c.nmats * c.N + 3) / 4;
-                if (blocks > 0x7FFFFFFF)
-                    return SKINNY_ERR_INVALID_ARG;
-                void *args[] = {&a, &nmats};
-                err = launch(sv->fn[c.M - 1], (int)blocks, 256, 0, args, stream);
-            } else {
-                if (lds > 65536 && !g_lds_raised[vidx][c.M - 1].load(std::memory_order_acquire)) {
-                    if (hipFuncSetAttribute(v->fn[c.M - 1], hipFuncAttributeMaxDynamicSharedMemorySize,
-                                            dev.max_lds) != hipSuccess)
-                        return SKINNY_ERR_LAUNCH;
-                    g_lds_raised[vidx][c.M - 1].store(1, std::memory_order_release);
-                }
-                if (plan.grid_blocks == 0) {
-                    const long long cap = (long long)dev.cus *
-                        blocks_per_cu(vidx, c.M, v->fn[c.M - 1], plan.threads_per_block, lds);
-                    if (cap < grid)
-                        grid = (int)cap;
-                }
-                void *args[] = {&a, &kpad};
-                err = launch(v->fn[c.M - 1], grid, plan.threads_per_block, lds, args, stream);
-            }
+            void *args[] = {&a};
+            err = launch(fn, grid, block, lds, args, stream);
         }
     }
     return err == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;

@@ -44,15 +44,18 @@ def log(msg):
     print(f"[sweep {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def candidate_plans(skg, K, M):
+def candidate_plans(skg, K, M, kinds=None):
     """Every (variant, block size, grid mode) able to run (K, M)."""
     out = []
     for v in skg.variants():
         d = v.as_dict()
-        if d["kind"] == skg.SKINNY_KIND_SCALAR:
+        if d["kind"] == skg.SKINNY_KIND_SCALAR or (kinds and d["kind"] not in kinds):
             continue
         if d["kind"] == skg.SKINNY_KIND_FIXED_K and \
                 d["k_split"] * d["lanes_per_row"] * 8 * d["chunks"] != K:
+            continue
+        if d["kind"] == skg.SKINNY_KIND_MFMA and \
+                (K % (128 * d["k_split"]) or (K // (128 * d["k_split"])) % d["chunks"]):
             continue
         for tpb in (128, 256, 512):
             if (tpb // 64) % d["k_split"]:
@@ -151,7 +154,8 @@ def measure(args):
                       else torch.empty((M, N), dtype=torch.bfloat16, device=dev))
                 nbytes = (4 * N * K + 2 * M * K + 4 * M * N) if pair else (2 * N * K + 2 * M * K + 2 * M * N)
                 best = None
-                for plan in candidate_plans(skg, K, M):
+                kinds = {int(k) for k in args.kinds.split(",")} if args.kinds else None
+                for plan in candidate_plans(skg, K, M, kinds):
                     try:
                         us, lo, hi = time_plan(torch, skg, x, weights, ys, plan, pair,
                                                args.trials, args.replays)
@@ -180,14 +184,16 @@ def pick(records, tol=0.005):
     return near[0]
 
 
-def emit_inc(path, out=INC_PATH):
+def emit_inc(paths, out=INC_PATH):
+    """Write the plan table from one or more sweep files (all records pooled)."""
     recs = {}
-    with open(path) as f:
-        for line in f:
-            r = json.loads(line)
-            if "plan" not in r:
-                continue
-            recs.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+    for path in paths.split(","):
+        with open(path) as f:
+            for line in f:
+                r = json.loads(line)
+                if "plan" not in r:
+                    continue
+                recs.setdefault((r["N"], r["K"], r["M"]), []).append(r)
     lines = [
         "// Tuned launch plans for gfx950, one line per (N, K, M):",
         "//   {N, K, M, {kind, threads_per_block, lanes_per_row, chunks, rows_per_wave, k_split,",
@@ -208,10 +214,12 @@ def emit_inc(path, out=INC_PATH):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--out", help="JSON-lines file to append measurements to")
-    ap.add_argument("--emit-inc", metavar="JSONL", help="write the plan table from a sweep file")
+    ap.add_argument("--emit-inc", metavar="JSONL[,JSONL...]",
+                    help="write the plan table from sweep files (records pooled)")
     ap.add_argument("--inc-path", default=INC_PATH)
     ap.add_argument("--only", help="comma list of NxK shapes to sweep")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
+    ap.add_argument("--kinds", help="comma list of plan kinds to time (default: all)")
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--replays", type=int, default=5)
     args = ap.parse_args()

@@ -68,7 +68,10 @@ typedef enum skinny_kind {
     SKINNY_KIND_FIXED_K = 1, /* K fixed at compile time = k_split*lanes_per_row*8*chunks;
                                 x in registers or LDS, tiles optionally software-pipelined */
     SKINNY_KIND_LOOP_K = 2,  /* any K % 8 == 0; x staged in LDS; chunks = loads in flight per row */
-    SKINNY_KIND_SCALAR = 3   /* any K, any alignment; element-wise loads */
+    SKINNY_KIND_SCALAR = 3,  /* any K, any alignment; element-wise loads */
+    SKINNY_KIND_MFMA = 4     /* K % (128*k_split*chunks) == 0; 4-row groups on the matrix
+                                cores (v_mfma_f32_4x4x4_16b_bf16), x staged in LDS,
+                                chunks = loads per group per K batch, lanes_per_row = 16 */
 } skinny_kind_t;
 
 /* One launch configuration ("plan"): the knobs of the plan tuple of vLLM PR
@@ -83,7 +86,7 @@ typedef struct skinny_plan {
                                   lane per row kept in flight (K unroll) */
     int32_t rows_per_wave;     /* row groups a wave processes per tile (outputs per wave =
                                   rows_per_wave * 64 / lanes_per_row) */
-    int32_t k_split;           /* waves of one block that split a row's K range (1, 2, 4);
+    int32_t k_split;           /* waves of one block that split a row's K range (1, 2, 4, 8);
                                   partial sums meet in LDS, summed in fixed order */
     int32_t nontemporal;       /* 1: W is read with the non-temporal cache hint */
     int32_t grid_blocks;       /* 0: a persistent grid that fills the device once (compute
@@ -91,11 +94,11 @@ typedef struct skinny_plan {
                                   tiles; > 0: at most this many blocks (a value >= the tile
                                   count gives one block per tile) */
     int32_t x_in_lds;          /* FIXED_K: 1 = x staged once per block in LDS, 0 = each lane
-                                  keeps its slice of x in registers; LOOP_K: always 1;
+                                  keeps its slice of x in registers; LOOP_K, MFMA: always 1;
                                   SCALAR: always 0 */
-    int32_t prefetch;          /* FIXED_K: 1 = the next tile's weights are loaded while the
-                                  current tile is consumed (two register sets); 0 = one tile
-                                  at a time; other kinds: always 0 */
+    int32_t prefetch;          /* FIXED_K, MFMA: 1 = the next tile's (MFMA: the next K batch's)
+                                  weights are loaded while the current one is consumed (two
+                                  register sets); 0 = one at a time; other kinds: always 0 */
 } skinny_plan_t;
 
 /* Checks that `device` is a gfx950 GPU and caches its properties. Optional:

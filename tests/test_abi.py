@@ -89,8 +89,8 @@ def test_variants_enumerate(skg):
         kinds.add(p.kind)
         assert p.threads_per_block % 64 == 0 and p.grid_blocks == 0
         assert p.lanes_per_row in (8, 16, 32, 64)
-        assert p.k_split in (1, 2, 4)
-    assert kinds == {1, 2, 3}
+        assert p.k_split in (1, 2, 4, 8)
+    assert kinds == {1, 2, 3, 4}
     with pytest.raises(skg.SkinnyError):
         skg.skinny_gemm_get_variant(n)
     with pytest.raises(skg.SkinnyError):
@@ -107,9 +107,12 @@ def test_default_plans(skg):
                    (4096, 8192), (77440, 4096), (4096, 128)]:
         for M in (1, 2, 3, 4):
             p, _ = skg.skinny_gemm_get_plan(N, K, M)
-            assert p.kind in (skg.SKINNY_KIND_FIXED_K, skg.SKINNY_KIND_LOOP_K), (N, K, M, p)
+            assert p.kind in (skg.SKINNY_KIND_FIXED_K, skg.SKINNY_KIND_LOOP_K,
+                              skg.SKINNY_KIND_MFMA), (N, K, M, p)
             if p.kind == skg.SKINNY_KIND_FIXED_K:
                 assert _fixed_k(p) == K
+            if p.kind == skg.SKINNY_KIND_MFMA:
+                assert K % (128 * p.k_split) == 0 and (K // (128 * p.k_split)) % p.chunks == 0
     # an unlisted K that a compile-time-K variant covers gets that variant by default
     p, tuned = skg.skinny_gemm_get_plan(1000, 4096, 1)
     assert not tuned and p.kind == skg.SKINNY_KIND_FIXED_K and _fixed_k(p) == 4096
@@ -140,6 +143,8 @@ def test_plan_table_entries_are_valid(skg):
                 p.x_in_lds, p.prefetch) in vset
         if p.kind == skg.SKINNY_KIND_FIXED_K:
             assert _fixed_k(p) == K
+        if p.kind == skg.SKINNY_KIND_MFMA:
+            assert K % (128 * p.k_split) == 0 and (K // (128 * p.k_split)) % p.chunks == 0
         assert 1 <= M <= 4 and p.threads_per_block // 64 % p.k_split == 0
 
 
