@@ -9,7 +9,8 @@ device is not gfx950, calls raise.
 Raw entry points (same names and arguments as the C functions; pointers as
 Python ints; a non-zero status raises :class:`SkinnyError`):
     skinny_gemm_init, skinny_gemm_bf16, skinny_gemm_bf16_pair,
-    skinny_gemm_bf16_ex, skinny_gemm_bf16_pair_ex, skinny_gemm_get_plan,
+    skinny_gemm_bf16_ex, skinny_gemm_bf16_pair_ex, skinny_gemm_bf16_f32out,
+    skinny_gemm_bf16_f32out_ex, skinny_gemm_get_plan,
     skinny_gemm_num_variants, skinny_gemm_get_variant,
     skinny_gemm_status_string, skinny_gemm_version
 
@@ -94,6 +95,8 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_bf16_pair.argtypes = [vp, vp, vp, vp, vp, i, i, i, vp]
         L.skinny_gemm_bf16_ex.argtypes = [vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_bf16_pair_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, pp, vp]
+        L.skinny_gemm_bf16_f32out.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.skinny_gemm_bf16_f32out_ex.argtypes = [vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_get_plan.argtypes = [i, i, i, pp]
         L.skinny_gemm_num_variants.argtypes = []
         L.skinny_gemm_get_variant.argtypes = [i, pp]
@@ -101,7 +104,8 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_status_string.restype = ctypes.c_char_p
         L.skinny_gemm_version.argtypes = []
         for name in ("skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair",
-                     "skinny_gemm_bf16_ex", "skinny_gemm_bf16_pair_ex", "skinny_gemm_get_plan",
+                     "skinny_gemm_bf16_ex", "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out",
+                     "skinny_gemm_bf16_f32out_ex", "skinny_gemm_get_plan",
                      "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -146,6 +150,16 @@ def skinny_gemm_bf16_pair_ex(x: int, W0: int, W1: int, y0: int, y1: int, M: int,
                              plan: Plan, stream: int = 0) -> None:
     _check(lib().skinny_gemm_bf16_pair_ex(x, W0, W1, y0, y1, M, N, K, ctypes.byref(plan), stream),
            "skinny_gemm_bf16_pair_ex")
+
+
+def skinny_gemm_bf16_f32out(x: int, W: int, y: int, M: int, N: int, K: int, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_f32out(x, W, y, M, N, K, stream), "skinny_gemm_bf16_f32out")
+
+
+def skinny_gemm_bf16_f32out_ex(x: int, W: int, y: int, M: int, N: int, K: int, plan: Plan,
+                               stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_f32out_ex(x, W, y, M, N, K, ctypes.byref(plan), stream),
+           "skinny_gemm_bf16_f32out_ex")
 
 
 def skinny_gemm_get_plan(N: int, K: int, M: int) -> tuple[Plan, bool]:
@@ -197,9 +211,10 @@ def _check_tensor(t: torch.Tensor, name: str, ndim: int = 2) -> None:
 
 
 def gemm(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
-         plan: Plan | None = None) -> torch.Tensor:
+         plan: Plan | None = None, out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """y = x @ W.T for bfloat16 x [M, K] (M <= 4) and W [N, K]; one kernel launch
-    on the current stream."""
+    on the current stream. out_dtype torch.float32 keeps the float32 sums
+    (skinny_gemm_bf16_f32out)."""
     _check_tensor(x, "x")
     _check_tensor(W, "W")
     M, K = x.shape
@@ -208,15 +223,24 @@ def gemm(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
         raise ValueError(f"inner sizes differ: x {tuple(x.shape)}, W {tuple(W.shape)}")
     if W.device != x.device:
         raise ValueError("x and W must be on the same device")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"out_dtype must be bfloat16 or float32, got {out_dtype}")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     else:
-        _check_tensor(out, "out")
-        if tuple(out.shape) != (M, N) or out.device != x.device:
-            raise ValueError(f"out must be [{M}, {N}] on {x.device}")
+        if out.dtype != out_dtype or out.device != x.device or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous {out_dtype} tensor on {x.device}")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be [{M}, {N}]")
     s = _stream_handle(x.device)
     with torch.cuda.device(x.device):
-        if plan is None:
+        if out_dtype == torch.float32:
+            if plan is None:
+                skinny_gemm_bf16_f32out(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, s)
+            else:
+                skinny_gemm_bf16_f32out_ex(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K,
+                                           plan, s)
+        elif plan is None:
             skinny_gemm_bf16(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, s)
         else:
             skinny_gemm_bf16_ex(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, plan, s)
@@ -257,7 +281,8 @@ def gemm_pair(x: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
 __all__ = [
     "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair",
     "skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",
-    "skinny_gemm_bf16_pair_ex", "skinny_gemm_get_plan", "skinny_gemm_num_variants",
+    "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out", "skinny_gemm_bf16_f32out_ex",
+    "skinny_gemm_get_plan", "skinny_gemm_num_variants",
     "skinny_gemm_get_variant", "skinny_gemm_status_string", "skinny_gemm_version",
     "SKINNY_OK", "SKINNY_ERR_INVALID_ARG", "SKINNY_ERR_UNSUPPORTED", "SKINNY_ERR_NOT_INITIALIZED",
     "SKINNY_ERR_LAUNCH", "SKINNY_KIND_FIXED_K", "SKINNY_KIND_LOOP_K", "SKINNY_KIND_SCALAR",

@@ -159,13 +159,23 @@ struct Args {
     const uint16_t *x;
     const uint16_t *w0;
     const uint16_t *w1;  // second weight of the pair (== w0 when nmats == 1)
-    uint16_t *y0;
-    uint16_t *y1;
+    void *y0;            // bfloat16 or float32 outputs, see out_f32
+    void *y1;
     int N;
     int K;
     int tiles_per_mat;   // ceil(N / rows per tile)
     int total_tiles;     // nmats * tiles_per_mat
+    int out_f32;         // 1: y is float32 (the sum, rounded once to float32); 0: bfloat16
 };
+
+// Store one output element: bfloat16 (nearest-even) or float32, by a block-uniform flag.
+__device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, float v)
+{
+    if (a.out_f32)
+        static_cast<float *>(ym)[idx] = v;
+    else
+        static_cast<uint16_t *>(ym)[idx] = f32_to_bf16(v);
+}
 
 // ---------------------------------------------------------------------------
 // Family FIXED_K: K = KW * LPR * 8 * CH known at compile time.
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 acc[m][r] = group_sum<LPR>(acc[m][r]);
 
         const int mat = t >= a.tiles_per_mat ? 1 : 0;
-        uint16_t *ym = mat ? a.y1 : a.y0;
+        void *ym = mat ? a.y1 : a.y0;
         const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
         if constexpr (KW == 1) {
             if (kl == OUT) {
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                     if (row < a.N) {
 #pragma unroll
                         for (int m = 0; m < M; ++m)
-                            ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m][r]);
+                            store_out(a, ym, (size_t)m * a.N + row, acc[m][r]);
                     }
                 }
             }
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 #pragma unroll
                             for (int q = 1; q < KW; ++q)
                                 s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
-                            ym[(size_t)m * a.N + row] = f32_to_bf16(s);
+                            store_out(a, ym, (size_t)m * a.N + row, s);
                         }
                     }
                 }
@@ -401,7 +411,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
         const int mat = tile >= a.tiles_per_mat ? 1 : 0;
         const int t = tile - mat * a.tiles_per_mat;
         const uint16_t *wm = mat ? a.w1 : a.w0;
-        uint16_t *ym = mat ? a.y1 : a.y0;
+        void *ym = mat ? a.y1 : a.y0;
         const int row0 = t * rows_t + wave * R;
         int valid = a.N - row0;
         valid = valid < 0 ? 0 : (valid > R ? R : valid);
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
                 if (row < a.N) {
 #pragma unroll
                     for (int m = 0; m < M; ++m)
-                        ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m][r]);
+                        store_out(a, ym, (size_t)m * a.N + row, acc[m][r]);
                 }
             }
         }
@@ -577,7 +587,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 
     auto finish = [&](int t) {
         const int mat = t >= a.tiles_per_mat ? 1 : 0;
-        uint16_t *ym = mat ? a.y1 : a.y0;
+        void *ym = mat ? a.y1 : a.y0;
         const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
         float s[R][M];
 #pragma unroll
@@ -593,7 +603,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
                     if (row < a.N) {
 #pragma unroll
                         for (int m = 0; m < M; ++m)
-                            ym[(size_t)m * a.N + row] = f32_to_bf16(s[r][m]);
+                            store_out(a, ym, (size_t)m * a.N + row, s[r][m]);
                     }
                 }
             }
@@ -618,7 +628,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 #pragma unroll
                             for (int q = 1; q < KW; ++q)
                                 v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
-                            ym[(size_t)m * a.N + row] = f32_to_bf16(v);
+                            store_out(a, ym, (size_t)m * a.N + row, v);
                         }
                     }
                 }
@@ -680,7 +690,7 @@ __global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
     const int mat = g >= a.N ? 1 : 0;
     const int row = (int)(g - (long long)mat * a.N);
     const uint16_t *w = (mat ? a.w1 : a.w0) + (size_t)row * a.K;
-    uint16_t *ym = mat ? a.y1 : a.y0;
+    void *ym = mat ? a.y1 : a.y0;
 
     float acc[M];
 #pragma unroll
@@ -698,18 +708,24 @@ __global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
     if (lane == sum_lane<64>()) {
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            ym[(size_t)m * a.N + row] = f32_to_bf16(acc[m]);
+            store_out(a, ym, (size_t)m * a.N + row, acc[m]);
     }
 }
 
-// K == 0: the empty sum, +0 everywhere.
-__global__ __launch_bounds__(256) void zero_kernel(uint16_t *y0, uint16_t *y1, long long count)
+// K == 0: the empty sum, +0 everywhere; `count` elements of `elem_bytes` (2 or 4) each.
+__global__ __launch_bounds__(256) void zero_kernel(void *y0, void *y1, long long count, int elem_bytes)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i < count) {
-        y0[i] = 0;
-        if (y1)
-            y1[i] = 0;
+        if (elem_bytes == 4) {
+            static_cast<float *>(y0)[i] = 0.0f;
+            if (y1)
+                static_cast<float *>(y1)[i] = 0.0f;
+        } else {
+            static_cast<uint16_t *>(y0)[i] = 0;
+            if (y1)
+                static_cast<uint16_t *>(y1)[i] = 0;
+        }
     }
 }
 

@@ -309,6 +309,7 @@ struct Call {
     const void *x, *w0, *w1;
     void *y0, *y1;
     int M, N, K, nmats;
+    int out_f32;  // 1: float32 outputs, 0: bfloat16
 };
 
 int validate(const Call &c)
@@ -325,7 +326,10 @@ int validate(const Call &c)
     for (const void *p : ptrs)
         if (p && !aligned(p, 2))
             return SKINNY_ERR_INVALID_ARG;
-    const size_t xb = (size_t)c.M * c.K * 2, wb = (size_t)c.N * c.K * 2, yb = (size_t)c.M * c.N * 2;
+    const size_t ye = c.out_f32 ? 4 : 2;
+    if (c.out_f32 && (!aligned(c.y0, 4) || (c.nmats == 2 && !aligned(c.y1, 4))))
+        return SKINNY_ERR_INVALID_ARG;
+    const size_t xb = (size_t)c.M * c.K * 2, wb = (size_t)c.N * c.K * 2, yb = (size_t)c.M * c.N * ye;
     for (int i = 0; i < c.nmats; ++i) {
         void *y = i ? c.y1 : c.y0;
         if (overlaps(y, yb, c.x, xb) || overlaps(y, yb, c.w0, wb) ||
@@ -454,9 +458,10 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
 
     if (c.K == 0) {
         long long count = (long long)c.M * c.N;
-        uint16_t *y0 = static_cast<uint16_t *>(c.y0);
-        uint16_t *y1 = c.nmats == 2 ? static_cast<uint16_t *>(c.y1) : nullptr;
-        void *args[] = {&y0, &y1, &count};
+        void *y0 = c.y0;
+        void *y1 = c.nmats == 2 ? c.y1 : nullptr;
+        int elem = c.out_f32 ? 4 : 2;
+        void *args[] = {&y0, &y1, &count, &elem};
         const long long blocks = (count + 255) / 256;
         if (blocks > 0x7FFFFFFF)
             return SKINNY_ERR_INVALID_ARG;
@@ -493,10 +498,11 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
     a.x = static_cast<const uint16_t *>(c.x);
     a.w0 = static_cast<const uint16_t *>(c.w0);
     a.w1 = static_cast<const uint16_t *>(c.nmats == 2 ? c.w1 : c.w0);
-    a.y0 = static_cast<uint16_t *>(c.y0);
-    a.y1 = static_cast<uint16_t *>(c.nmats == 2 ? c.y1 : c.y0);
+    a.y0 = c.y0;
+    a.y1 = c.nmats == 2 ? c.y1 : c.y0;
     a.N = c.N;
     a.K = c.K;
+    a.out_f32 = c.out_f32;
 
     const int vidx = (int)(v - kAllVariants);
     hipError_t err;
@@ -586,7 +592,7 @@ int skinny_gemm_init(int device) { return check_device(device, nullptr); }
 
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N, int K, hipStream_t stream)
 {
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1}, nullptr, stream);
+    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 0}, nullptr, stream);
 }
 
 int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1, void *y0, void *y1, int M,
@@ -594,7 +600,7 @@ int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1, void *y
 {
     if (!W1 && K > 0 && M > 0 && N > 0)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W0, W1, y0, y1, M, N, K, 2}, nullptr, stream);
+    return run(Call{x, W0, W1, y0, y1, M, N, K, 2, 0}, nullptr, stream);
 }
 
 int skinny_gemm_bf16_ex(const void *x, const void *W, void *y, int M, int N, int K,
@@ -602,7 +608,7 @@ int skinny_gemm_bf16_ex(const void *x, const void *W, void *y, int M, int N, int
 {
     if (!plan)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1}, plan, stream);
+    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 0}, plan, stream);
 }
 
 int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1, void *y0, void *y1,
@@ -610,7 +616,21 @@ int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1, void
 {
     if (!plan)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W0, W1, y0, y1, M, N, K, 2}, plan, stream);
+    return run(Call{x, W0, W1, y0, y1, M, N, K, 2, 0}, plan, stream);
+}
+
+int skinny_gemm_bf16_f32out(const void *x, const void *W, float *y, int M, int N, int K,
+                            hipStream_t stream)
+{
+    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 1}, nullptr, stream);
+}
+
+int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y, int M, int N, int K,
+                               const skinny_plan_t *plan, hipStream_t stream)
+{
+    if (!plan)
+        return SKINNY_ERR_INVALID_ARG;
+    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 1}, plan, stream);
 }
 
 int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out)

@@ -29,11 +29,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 INC_PATH = os.path.join(HERE, "csrc", "plans_gfx950.inc")
 ROTATE_BYTES = 1 << 30
 
-# The decode projections at M = 1, 2, 4 (and 3, which the API supports), plus the
-# paired (4096, 128) f_b/g_b weights, which are swept as pairs.
+# The decode projections at M = 1, 2, 4 (and 3, which the API supports): the TP=2
+# rank shapes of vLLM PR #62949 (section Validation), the TP4/TP8 rank shapes of
+# vLLM PR #65306 (section Validation: LM head / KDA in_proj rows (6416, 4096),
+# (19360, 4096), (38720, 4096)) and the router gate (288, 4096) (float32 output; it
+# shares the bf16 plan). Paired f_b/g_b weights (4096, 128) and the TP4 pair
+# (2048, 128) are swept as pairs.
 SHAPES = [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536), (4096, 8192),
-          (77440, 4096)]
-PAIR_SHAPES = [(4096, 128)]
+          (77440, 4096), (6416, 4096), (19360, 4096), (38720, 4096), (288, 4096)]
+PAIR_SHAPES = [(4096, 128), (2048, 128)]
 MS = (1, 2, 3, 4)
 BIG_GRID = 1 << 30  # grid_blocks >= tile count: one block per tile
 PLAN_FIELDS = ("kind", "threads_per_block", "lanes_per_row", "chunks", "rows_per_wave", "k_split",

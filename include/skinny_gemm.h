@@ -135,6 +135,18 @@ int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1,
                              void *y0, void *y1, int M, int N, int K,
                              const skinny_plan_t *plan, hipStream_t stream);
 
+/* y = x . W^T with float32 outputs: the float32 accumulation is stored without the
+ * bfloat16 rounding. This is the epilogue of the router gate (288, 4096), the one
+ * BF16-input projection with an fp32 output that vLLM PR #62949 (SM121 skinny GEMM
+ * plans), section Validation, leaves on cuBLAS. x and W as in skinny_gemm_bf16; y
+ * is a DEVICE pointer to M*N float32 values, row-major [M][N], 4-byte aligned, not
+ * overlapping x or W. Same plans, sizes, errors and stream semantics as
+ * skinny_gemm_bf16 / skinny_gemm_bf16_ex (K == 0 writes +0.0f). */
+int skinny_gemm_bf16_f32out(const void *x, const void *W, float *y,
+                            int M, int N, int K, hipStream_t stream);
+int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y,
+                               int M, int N, int K, const skinny_plan_t *plan, hipStream_t stream);
+
 /* The plan skinny_gemm_bf16 would use for (N, K, M) with 16-byte aligned
  * pointers. Writes *out; returns 1 if it comes from the tuned table, 0 if it is
  * the default plan, or SKINNY_ERR_INVALID_ARG. Host-only: needs no device. */

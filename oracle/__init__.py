@@ -136,6 +136,14 @@ def gemm(x_bits, W_bits, nthreads: int | None = None):
     return gemm_rows(x_bits, W_bits, None, nthreads)
 
 
+def gemm_f32out(x_bits, W_bits, rows=None, nthreads: int | None = None):
+    """Oracle for the float32-output form: the same float64 sum, rounded once to
+    float32 (IEEE round-to-nearest-even, numpy's float64 -> float32 conversion).
+    Returns (y32 [M, R] float32, ref64, mag)."""
+    _, ref64, mag = gemm_rows(x_bits, W_bits, rows, nthreads)
+    return ref64.astype(np.float32), ref64, mag
+
+
 def gemm_pair(x_bits, W0_bits, W1_bits, nthreads: int | None = None):
     """Paired form: the same definition applied to W0 and to W1 with one shared x."""
     return gemm(x_bits, W0_bits, nthreads), gemm(x_bits, W1_bits, nthreads)

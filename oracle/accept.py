@@ -22,9 +22,22 @@ S1_ABS = 7.5e-5
 S1_REL = 2.0 ** -8
 
 
-def _f64(bits) -> np.ndarray:
-    b = np.ascontiguousarray(bits, dtype=np.uint16)
+def _f64(vals) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) or float32 values -> float64."""
+    a = np.asarray(vals)
+    if a.dtype == np.float32:
+        return a.astype(np.float64)
+    b = np.ascontiguousarray(a, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _n_bitwise_equal(a, b) -> int:
+    """Number of elements whose bit patterns agree (bf16 bits or float32 values)."""
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    if a.dtype == np.float32:
+        a, b = a.view(np.uint32), b.astype(np.float32).view(np.uint32)
+    return int(np.sum(a == b))
 
 
 def cosine_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
@@ -46,6 +59,9 @@ def cosine_rows(a: np.ndarray, b: np.ndarray) -> np.ndarray:
 
 def acceptance(y_bits, y_ref_bits, ref64, mag, check_cosine: bool = True) -> dict:
     """Evaluate G1, G2 and S1 for one [M, L] output block.
+
+    y_bits / y_ref_bits are bfloat16 bit patterns (uint16), or float32 values for
+    the float32-output form (both arrays of the same kind).
 
     Returns a dict with the pass flags and the worst margins: max_g1_ratio and
     max_s1_ratio are max(|err| / bound) (<= 1 passes), min_cos the smallest row
@@ -72,7 +88,7 @@ def acceptance(y_bits, y_ref_bits, ref64, mag, check_cosine: bool = True) -> dic
         "max_g1_ratio": g1_ratio,
         "max_s1_ratio": s1_ratio,
         "max_abs_err": float(np.max(err_g1)) if y.size else 0.0,
-        "n_bitwise_equal": int(np.sum(np.asarray(y_bits, np.uint16) == np.asarray(y_ref_bits, np.uint16))),
+        "n_bitwise_equal": _n_bitwise_equal(y_bits, y_ref_bits),
         "n": int(y.size),
     }
     if check_cosine:

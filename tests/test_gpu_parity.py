@@ -473,3 +473,83 @@ def test_weight_beyond_4gib(skg):
     assert res["pass"], res
     del Wd
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# float32-output form (router gate epilogue)
+# ---------------------------------------------------------------------------
+
+def check_f32(y_dev, x, W, rows=None, label=""):
+    y = y_dev.cpu().numpy()
+    assert y.dtype == np.float32
+    yr, ref, mag = oracle.gemm_f32out(x, W, rows)
+    yy = y if rows is None else y[:, rows]
+    res = oracle.acceptance(yy, yr, ref, mag, check_cosine=rows is None)
+    assert res["pass"], f"{label}: {res}"
+    return res
+
+
+@pytest.mark.parametrize("shape", [(288, 4096), (4096, 1024), (1000, 1536), (77, 1000), (33, 13),
+                                   (4096, 128)], ids=lambda s: f"{s[0]}x{s[1]}")
+def test_f32_output(skg, shape):
+    N, K = shape
+    W = synth.weights(N, K, seed=90, shape_id=N)
+    Wd = to_dev(W)
+    for M in (1, 2, 3, 4):
+        x = synth.activations(M, K, seed=90, shape_id=N, tensor_id=M)
+        xd = to_dev(x)
+        y = skg.gemm(xd, Wd, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        check_f32(y, x, W, label=f"f32 N={N} K={K} M={M}")
+        # the bf16 output is the same float32 sum rounded to nearest-even
+        p, _ = skg.skinny_gemm_get_plan(N, K, M)
+        if K % 8 == 0:
+            yb = skg.gemm(xd, Wd, plan=p)
+            y32 = skg.gemm(xd, Wd, plan=p, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            assert torch.equal(yb.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
+def test_f32_output_every_variant(skg):
+    M = 2
+    for p in skg.variants():
+        K = variant_K(p)[0]
+        N = 2 * rows_per_tile(p) + 3
+        x = synth.activations(M, K, seed=91, shape_id=K)
+        W = synth.weights(N, K, seed=91, shape_id=K)
+        try:
+            y = skg.gemm(to_dev(x), to_dev(W), plan=p, out_dtype=torch.float32)
+        except skg.SkinnyError as e:
+            assert e.status == skg.SKINNY_ERR_UNSUPPORTED and p.kind == 1, str(e)
+            continue
+        torch.cuda.synchronize()
+        check_f32(y, x, W, label=f"f32 {p}")
+
+
+def test_f32_output_exact_and_empty(skg):
+    g = np.random.default_rng(92)
+    K, N = 4096, 300
+    xi = synth.small_int_bf16((4, K), -1, 1, g)
+    Wi = synth.small_int_bf16((N, K), -1, 1, g)
+    Wi[:, 256:] = 0  # |sum| <= 256: every partial sum exact in float32
+    y = skg.gemm(to_dev(xi), to_dev(Wi), out_dtype=torch.float32).cpu().numpy()
+    yr, _, _ = oracle.gemm_f32out(xi, Wi)
+    np.testing.assert_array_equal(y, yr)
+    # K == 0 writes +0.0f
+    y = torch.full((3, 50), 5.0, dtype=torch.float32, device="cuda")
+    skg.gemm(torch.empty((3, 0), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((50, 0), dtype=torch.bfloat16, device="cuda"), out=y,
+             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.all(y.view(torch.int32) == 0)
+
+
+def test_f32_output_rejects_misaligned(skg):
+    x = torch.zeros((1, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    st = skg.lib().skinny_gemm_bf16_f32out(x.data_ptr(), W.data_ptr(), buf.data_ptr() + 2,
+                                           1, 8, 64, None)
+    assert st == skg.SKINNY_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(buf == 0)

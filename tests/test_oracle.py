@@ -284,6 +284,44 @@ def test_empty_shapes(oracle_mod):
     assert y.shape == (1, 0)
 
 
+def test_f32_output_form(oracle_mod):
+    """The float32-output oracle: the same double sum, rounded once to float32."""
+    def b(v):
+        return synth.f32_to_bf16_bits(np.array(v, np.float32))
+    # exact double sums 1 + 2^-24 (float32 tie -> 1.0) and 1 + 3*2^-24 (tie -> 1 + 2^-22)
+    x = np.zeros((2, 3), np.uint16)
+    x[0] = b([1.0, 2.0 ** -12, 0.0])
+    x[1] = b([1.0, 2.0 ** -12, 2.0 ** -11])
+    W = np.zeros((1, 3), np.uint16)
+    W[0] = b([1.0, 2.0 ** -12, 2.0 ** -12])
+    y32, ref64, _ = oracle_mod.gemm_f32out(x, W)
+    assert ref64[0, 0] == 1.0 + 2.0 ** -24 and ref64[1, 0] == 1.0 + 3 * 2.0 ** -24
+    assert y32.dtype == np.float32
+    assert y32[0, 0] == np.float32(1.0)
+    assert y32[1, 0] == np.float32(1.0 + 2.0 ** -22)
+    # just above a tie goes up (1 + 2^-24 + 2^-40 is exact in double)
+    x2 = np.zeros((1, 4), np.uint16)
+    x2[0] = b([1.0, 2.0 ** -12, 2.0 ** -20, 0.0])
+    W2 = np.zeros((1, 4), np.uint16)
+    W2[0] = b([1.0, 2.0 ** -12, 2.0 ** -20, 0.0])
+    y32b, _, _ = oracle_mod.gemm_f32out(x2, W2)
+    assert y32b[0, 0] == np.float32(1.0 + 2.0 ** -23)
+    # small-integer products: exact
+    g = np.random.default_rng(21)
+    xi = synth.small_int_bf16((3, 40), -3, 3, g)
+    Wi = synth.small_int_bf16((17, 40), -3, 3, g)
+    y32, ref64, _ = oracle_mod.gemm_f32out(xi, Wi)
+    exact = np.rint(_f64_of_bits(xi)).astype(np.int64) @ np.rint(_f64_of_bits(Wi)).astype(np.int64).T
+    np.testing.assert_array_equal(y32, exact.astype(np.float32))
+    # the bf16 output is the same sum rounded differently
+    ybf, _, _ = oracle_mod.gemm(xi, Wi)
+    np.testing.assert_array_equal(_f64_of_bits(ybf), exact.astype(np.float64))
+    # selected rows
+    rows = np.array([3, 0, 16], np.int64)
+    y32r, _, _ = oracle_mod.gemm_f32out(xi, Wi, rows)
+    np.testing.assert_array_equal(y32r, y32[:, rows])
+
+
 # ----------------------------------------------------------------------------
 # Acceptance rules
 # ----------------------------------------------------------------------------
@@ -310,3 +348,10 @@ def test_acceptance_rules(oracle_mod):
     y4 = y.copy()
     y4[0, :] = 0
     assert not accept.acceptance(y4, y, ref64, mag)["g2_pass"]
+    # float32 outputs are compared as values
+    y32, _, _ = oracle_mod.gemm_f32out(x, W)
+    r32 = accept.acceptance(y32, y32, ref64, mag)
+    assert r32["pass"] and r32["n_bitwise_equal"] == y32.size
+    y32b = y32.copy()
+    y32b[1, 3] = -y32b[1, 3] - 1.0
+    assert not accept.acceptance(y32b, y32, ref64, mag)["pass"]
