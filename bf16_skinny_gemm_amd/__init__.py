@@ -9,12 +9,13 @@ device is not gfx950, calls raise.
 Raw entry points (same names and arguments as the C functions; pointers as
 Python ints; a non-zero status raises :class:`SkinnyError`):
     skinny_gemm_init, skinny_gemm_bf16, skinny_gemm_bf16_pair,
-    skinny_gemm_bf16_ex, skinny_gemm_bf16_pair_ex, skinny_gemm_bf16_f32out,
+    skinny_gemm_bf16_ex, skinny_gemm_bf16_pair_ex, skinny_gemm_bf16_pair_strided,
+    skinny_gemm_bf16_pair_strided_ex, skinny_gemm_bf16_f32out,
     skinny_gemm_bf16_f32out_ex, skinny_gemm_get_plan,
     skinny_gemm_num_variants, skinny_gemm_get_variant,
     skinny_gemm_status_string, skinny_gemm_version
 
-Tensor helpers: :func:`gemm` and :func:`gemm_pair`.
+Tensor helpers: :func:`gemm`, :func:`gemm_pair` and :func:`gemm_pair_strided`.
 """
 from __future__ import annotations
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_bf16_ex.argtypes = [vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_bf16_pair_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_bf16_f32out.argtypes = [vp, vp, vp, i, i, i, vp]
+        L.skinny_gemm_bf16_pair_strided.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, vp]
+        L.skinny_gemm_bf16_pair_strided_ex.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, pp, vp]
         L.skinny_gemm_bf16_f32out_ex.argtypes = [vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_get_plan.argtypes = [i, i, i, pp]
         L.skinny_gemm_num_variants.argtypes = []
@@ -105,7 +108,8 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_version.argtypes = []
         for name in ("skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair",
                      "skinny_gemm_bf16_ex", "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out",
-                     "skinny_gemm_bf16_f32out_ex", "skinny_gemm_get_plan",
+                     "skinny_gemm_bf16_f32out_ex", "skinny_gemm_bf16_pair_strided",
+                     "skinny_gemm_bf16_pair_strided_ex", "skinny_gemm_get_plan",
                      "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -150,6 +154,20 @@ def skinny_gemm_bf16_pair_ex(x: int, W0: int, W1: int, y0: int, y1: int, M: int,
                              plan: Plan, stream: int = 0) -> None:
     _check(lib().skinny_gemm_bf16_pair_ex(x, W0, W1, y0, y1, M, N, K, ctypes.byref(plan), stream),
            "skinny_gemm_bf16_pair_ex")
+
+
+def skinny_gemm_bf16_pair_strided(x0: int, x1: int, ldx: int, W0: int, W1: int, y0: int, y1: int,
+                                  ldy: int, M: int, N: int, K: int, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_pair_strided(x0, x1, ldx, W0, W1, y0, y1, ldy, M, N, K, stream),
+           "skinny_gemm_bf16_pair_strided")
+
+
+def skinny_gemm_bf16_pair_strided_ex(x0: int, x1: int, ldx: int, W0: int, W1: int, y0: int, y1: int,
+                                     ldy: int, M: int, N: int, K: int, plan: Plan,
+                                     stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_pair_strided_ex(x0, x1, ldx, W0, W1, y0, y1, ldy, M, N, K,
+                                                  ctypes.byref(plan), stream),
+           "skinny_gemm_bf16_pair_strided_ex")
 
 
 def skinny_gemm_bf16_f32out(x: int, W: int, y: int, M: int, N: int, K: int, stream: int = 0) -> None:
@@ -278,8 +296,57 @@ def gemm_pair(x: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
     return outs[0], outs[1]
 
 
+def _check_rowview(t: torch.Tensor, name: str) -> None:
+    """A 2-D bfloat16 GPU view with unit column stride (rows may be strided)."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a bfloat16 GPU tensor")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride, got stride {t.stride()}")
+
+
+def gemm_pair_strided(x0: torch.Tensor, x1: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
+                      out0: torch.Tensor | None = None, out1: torch.Tensor | None = None,
+                      plan: Plan | None = None) -> tuple[torch.Tensor, torch.Tensor]:
+    """(x0 @ W0.T, x1 @ W1.T) in one launch, x0 and x1 being row-strided views with
+    the same row stride (e.g. the two halves of a merged [M, 2K] activation); out0
+    and out1 may likewise be views of one merged [M, 2N] output."""
+    _check_rowview(x0, "x0")
+    _check_rowview(x1, "x1")
+    _check_tensor(W0, "W0")
+    _check_tensor(W1, "W1")
+    M, K = x0.shape
+    if tuple(x1.shape) != (M, K) or x1.stride(0) != x0.stride(0):
+        raise ValueError("x0 and x1 must have the same shape and row stride")
+    if tuple(W0.shape) != tuple(W1.shape) or W0.shape[1] != K:
+        raise ValueError(f"shapes: x {tuple(x0.shape)}, W0 {tuple(W0.shape)}, W1 {tuple(W1.shape)}")
+    N = W0.shape[0]
+    if out0 is None and out1 is None:
+        merged = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=x0.device)
+        out0, out1 = merged[:, :N], merged[:, N:]
+    elif out0 is None or out1 is None:
+        raise ValueError("give both out0 and out1, or neither")
+    for o, name in ((out0, "out0"), (out1, "out1")):
+        _check_rowview(o, name)
+        if tuple(o.shape) != (M, N):
+            raise ValueError(f"{name} must be [{M}, {N}]")
+    if out0.stride(0) != out1.stride(0):
+        raise ValueError("out0 and out1 must have the same row stride")
+    ldx = x0.stride(0) if M > 1 else K
+    ldy = out0.stride(0) if M > 1 else N
+    s = _stream_handle(x0.device)
+    with torch.cuda.device(x0.device):
+        args = (x0.data_ptr(), x1.data_ptr(), ldx, W0.data_ptr(), W1.data_ptr(), out0.data_ptr(),
+                out1.data_ptr(), ldy, M, N, K)
+        if plan is None:
+            skinny_gemm_bf16_pair_strided(*args, s)
+        else:
+            skinny_gemm_bf16_pair_strided_ex(*args, plan, s)
+    return out0, out1
+
+
 __all__ = [
-    "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair",
+    "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair", "gemm_pair_strided",
+    "skinny_gemm_bf16_pair_strided", "skinny_gemm_bf16_pair_strided_ex",
     "skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",
     "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out", "skinny_gemm_bf16_f32out_ex",
     "skinny_gemm_get_plan", "skinny_gemm_num_variants",

@@ -156,17 +156,40 @@ __device__ __forceinline__ float group_sum(float v)
 }
 
 struct Args {
-    const uint16_t *x;
+    const uint16_t *x;   // x of the first (or only) weight: row m at x + m * ldx
+    const uint16_t *x1;  // x of the second weight of a pair (== x when it is shared)
     const uint16_t *w0;
     const uint16_t *w1;  // second weight of the pair (== w0 when nmats == 1)
-    void *y0;            // bfloat16 or float32 outputs, see out_f32
+    void *y0;            // bfloat16 or float32 outputs, see out_f32; row m at y + m * ldy
     void *y1;
     int N;
     int K;
-    int tiles_per_mat;   // ceil(N / rows per tile)
-    int total_tiles;     // nmats * tiles_per_mat
+    int ldx;             // row stride of x and x1, in elements (>= K)
+    int ldy;             // row stride of y0 and y1, in elements (>= N)
+    int nmats;           // 1, or 2 for the paired form
+    int tiles;           // tiles per weight: ceil(N / rows per tile)
     int out_f32;         // 1: y is float32 (the sum, rounded once to float32); 0: bfloat16
 };
+
+// Which weight a block serves and which of its tiles: t = first, first + step, ...
+// For a pair, even blocks serve W0 and odd blocks W1 (the host launches an even
+// grid), so a block stages one x only.
+struct Sched {
+    int mat, first, step;
+};
+
+__device__ __forceinline__ Sched block_sched(const Args &a)
+{
+    if (a.nmats == 2)
+        return Sched{(int)(blockIdx.x & 1), (int)(blockIdx.x >> 1), (int)(gridDim.x >> 1)};
+    return Sched{0, (int)blockIdx.x, (int)gridDim.x};
+}
+
+// Bytes of x a block may read: M rows of K elements at stride ldx.
+__device__ __forceinline__ unsigned x_bytes(const Args &a, int M)
+{
+    return (unsigned)(((M - 1) * a.ldx + a.K) * 2);
+}
 
 // Store one output element: bfloat16 (nearest-even) or float32, by a block-uniform flag.
 __device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, float v)
@@ -191,7 +214,7 @@ __device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, f
 // multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
 // chunk reads its piece back, which frees VGPRs at M = 3, 4).
 //
-// Blocks loop over tiles tile = blockIdx.x, + gridDim.x, ... With PF the loop
+// Each block loops over the tiles of one weight (block_sched). With PF the loop
 // is software-pipelined: the loads of the next tile are issued before the
 // current one is consumed, so a wave pays the HBM latency once rather than once
 // per tile; a prefetch past the last tile uses an empty buffer resource and
@@ -209,18 +232,18 @@ struct FixedK {
     static_assert(64 % LPR == 0 && LPR >= 8, "lanes per row: 8, 16, 32 or 64");
     static_assert(kMaxWaves % KW == 0, "k_split must divide the largest block");
 
-    // Issue the weight loads of `tile` for this wave's rows.
-    static __device__ __forceinline__ void issue(const Args &a, int tile, int rows_t, int grp,
-                                                 int sub, unsigned kbase, u32x4 (&wv)[R][CH])
+    // Issue the weight loads of tile t of weight wm for this wave's rows; a tile
+    // past the last one gets an empty buffer resource and reads zeros.
+    static __device__ __forceinline__ void issue(const Args &a, const uint16_t *wm, int t, int rows_t,
+                                                 int grp, int sub, unsigned kbase, u32x4 (&wv)[R][CH])
     {
-        const uint16_t *base = a.w0;
+        const uint16_t *base = wm;
         int valid = 0;
-        if (tile < a.total_tiles) {
-            const int mat = tile >= a.tiles_per_mat ? 1 : 0;
-            const int row0 = (tile - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+        if (t < a.tiles) {
+            const int row0 = t * rows_t + grp * ROWS_W;
             valid = a.N - row0;
             valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
-            base = (mat ? a.w1 : a.w0) + (size_t)row0 * K;
+            base = wm + (size_t)row0 * K;
         }
         const __amdgpu_buffer_rsrc_t ws = make_rsrc(base, (unsigned)(valid * K * 2));
 #pragma unroll
@@ -251,31 +274,39 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     const int sub = lane / LPR;
     const int kl = lane % LPR;
     const unsigned kbase = (unsigned)(kw * KSLICE + kl * 8);
-    const int step = (int)gridDim.x;
+    const Sched sc = block_sched(a);
+    const int step = sc.step;
+    const uint16_t *wm = sc.mat ? a.w1 : a.w0;
+    const uint16_t *xm = sc.mat ? a.x1 : a.x;
+    void *ym = sc.mat ? a.y1 : a.y0;
 
-    int tile = blockIdx.x;
-    if (tile >= a.total_tiles)
+    int tile = sc.first;
+    if (tile >= a.tiles)
         return;  // whole block
 
     __shared__ u32x4 x_lds[XL ? M * K / 8 : 1];
     __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
     u32x4 wa[R][CH], wb[PF ? R : 1][PF ? CH : 1];
     u32x4 xr[XL ? 1 : M][XL ? 1 : CH];
-    const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(xm, x_bytes(a, M));
+    const int ldx = a.ldx;
     if constexpr (XL) {
-        // x pieces first (L2), then the weights (HBM), then x into LDS
-        auto src = [](int i) { return (unsigned)i * 16u; };
+        // x pieces first (L2), then the weights (HBM), then x into LDS as [M][K]
+        auto src = [=](int i) {
+            const int m = i / (K / 8);
+            return (unsigned)(m * ldx + (i - m * (K / 8)) * 8) * 2u;
+        };
         u32x4 xt[kStageBatch];
         stage_issue(xs, M * K / 8, src, xt);
-        F::issue(a, tile, rows_t, grp, sub, kbase, wa);
+        F::issue(a, wm, tile, rows_t, grp, sub, kbase, wa);
         stage_finish(xs, M * K / 8, src, xt, x_lds);
     } else {
-        F::issue(a, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
+        F::issue(a, wm, tile, rows_t, grp, sub, kbase, wa);  // weights first: they come from HBM
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll
             for (int j = 0; j < CH; ++j)
-                xr[m][j] = load16<false>(xs, (unsigned)(m * K + kbase + j * LPR * 8) * 2u);
+                xr[m][j] = load16<false>(xs, (unsigned)(m * ldx + (int)kbase + j * LPR * 8) * 2u);
     }
 
     auto consume = [&](int t, const u32x4 (&wv)[R][CH]) {
@@ -309,9 +340,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
             for (int r = 0; r < R; ++r)
                 acc[m][r] = group_sum<LPR>(acc[m][r]);
 
-        const int mat = t >= a.tiles_per_mat ? 1 : 0;
-        void *ym = mat ? a.y1 : a.y0;
-        const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+        const int row0 = t * rows_t + grp * ROWS_W;
         if constexpr (KW == 1) {
             if (kl == OUT) {
 #pragma unroll
@@ -320,7 +349,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                     if (row < a.N) {
 #pragma unroll
                         for (int m = 0; m < M; ++m)
-                            store_out(a, ym, (size_t)m * a.N + row, acc[m][r]);
+                            store_out(a, ym, (size_t)m * a.ldy + row, acc[m][r]);
                     }
                 }
             }
@@ -344,7 +373,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 #pragma unroll
                             for (int q = 1; q < KW; ++q)
                                 s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
-                            store_out(a, ym, (size_t)m * a.N + row, s);
+                            store_out(a, ym, (size_t)m * a.ldy + row, s);
                         }
                     }
                 }
@@ -356,24 +385,24 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     if constexpr (PF) {
         // Two register sets alternate: while one tile is consumed, the next is in flight.
         while (true) {
-            F::issue(a, tile + step, rows_t, grp, sub, kbase, wb);
+            F::issue(a, wm, tile + step, rows_t, grp, sub, kbase, wb);
             consume(tile, wa);
             tile += step;
-            if (tile >= a.total_tiles)
+            if (tile >= a.tiles)
                 break;
-            F::issue(a, tile + step, rows_t, grp, sub, kbase, wa);
+            F::issue(a, wm, tile + step, rows_t, grp, sub, kbase, wa);
             consume(tile, wb);
             tile += step;
-            if (tile >= a.total_tiles)
+            if (tile >= a.tiles)
                 break;
         }
     } else {
         while (true) {
             consume(tile, wa);
             tile += step;
-            if (tile >= a.total_tiles)
+            if (tile >= a.tiles)
                 break;
-            F::issue(a, tile, rows_t, grp, sub, kbase, wa);
+            F::issue(a, wm, tile, rows_t, grp, sub, kbase, wa);
         }
     }
 }
@@ -393,13 +422,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int K = a.K;
     const int kvec = kpad / 8;
+    const Sched sc = block_sched(a);
+    if (sc.first >= a.tiles)
+        return;  // whole block
+    const uint16_t *wm = sc.mat ? a.w1 : a.w0;
+    void *ym = sc.mat ? a.y1 : a.y0;
 
     {
-        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+        const __amdgpu_buffer_rsrc_t xs = make_rsrc(sc.mat ? a.x1 : a.x, x_bytes(a, M));
+        const int ldx = a.ldx;
         auto src = [=](int i) {
             const int m = i / kvec;
             const int kv = i - m * kvec;
-            return kv * 8 < K ? (unsigned)(m * K + kv * 8) * 2u : kOutOfRange;
+            return kv * 8 < K ? (unsigned)(m * ldx + kv * 8) * 2u : kOutOfRange;
         };
         u32x4 xt[kStageBatch];
         stage_issue(xs, M * kvec, src, xt);
@@ -407,11 +442,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
     }
 
     const int rows_t = (int)(blockDim.x >> 6) * R;
-    for (int tile = blockIdx.x; tile < a.total_tiles; tile += gridDim.x) {
-        const int mat = tile >= a.tiles_per_mat ? 1 : 0;
-        const int t = tile - mat * a.tiles_per_mat;
-        const uint16_t *wm = mat ? a.w1 : a.w0;
-        void *ym = mat ? a.y1 : a.y0;
+    for (int t = sc.first; t < a.tiles; t += sc.step) {
         const int row0 = t * rows_t + wave * R;
         int valid = a.N - row0;
         valid = valid < 0 ? 0 : (valid > R ? R : valid);
@@ -460,7 +491,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
                 if (row < a.N) {
 #pragma unroll
                     for (int m = 0; m < M; ++m)
-                        store_out(a, ym, (size_t)m * a.N + row, acc[m][r]);
+                        store_out(a, ym, (size_t)m * a.ldy + row, acc[m][r]);
                 }
             }
         }
@@ -519,22 +550,24 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
     const int lj = lane & 3;   // row of A / column of B and D within a block
     const int lb = lane >> 2;  // block: which 8-element K chunk
     const int xrow = lj < M ? lj : 0;
-    const int step = (int)gridDim.x;
+    const Sched sc = block_sched(a);
+    const int step = sc.step;
+    const uint16_t *wm = sc.mat ? a.w1 : a.w0;
+    void *ym = sc.mat ? a.y1 : a.y0;
 
-    int tile = blockIdx.x;
-    if (tile >= a.total_tiles)
+    int tile = sc.first;
+    if (tile >= a.tiles)
         return;  // whole block
 
-    // W loads of batch b of tile t for this wave's R groups.
+    // W loads of batch b of tile t for this wave's R groups (empty past the last tile).
     auto issue = [&](int t, int b, u32x4 (&wv)[R][U]) {
-        const uint16_t *base = a.w0;
+        const uint16_t *base = wm;
         int valid = 0;
-        if (t < a.total_tiles) {
-            const int mat = t >= a.tiles_per_mat ? 1 : 0;
-            const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+        if (t < a.tiles) {
+            const int row0 = t * rows_t + grp * ROWS_W;
             valid = a.N - row0;
             valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
-            base = (mat ? a.w1 : a.w0) + (size_t)row0 * K;
+            base = wm + (size_t)row0 * K;
         }
         const __amdgpu_buffer_rsrc_t ws = make_rsrc(base, (unsigned)(valid * K * 2));
         const unsigned k0 = (unsigned)(kw * kslice + b * 128 * U + lb * 8);
@@ -547,13 +580,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 
     u32x4 wa[R][U], wb[PF ? R : 1][PF ? U : 1];
     {
-        // x pieces first (L2), then the weights (HBM), then x into LDS
-        const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
-        auto src = [](int i) { return (unsigned)i * 16u; };
+        // x pieces first (L2), then the weights (HBM), then x into LDS as [M][K]
+        const __amdgpu_buffer_rsrc_t xs = make_rsrc(sc.mat ? a.x1 : a.x, x_bytes(a, M));
+        const int ldx = a.ldx;
+        const int kv8 = K / 8;
+        auto src = [=](int i) {
+            const int m = i / kv8;
+            return (unsigned)(m * ldx + (i - m * kv8) * 8) * 2u;
+        };
         u32x4 xt[kStageBatch];
-        stage_issue(xs, M * K / 8, src, xt);
+        stage_issue(xs, M * kv8, src, xt);
         issue(tile, 0, wa);
-        stage_finish(xs, M * K / 8, src, xt, mx_lds);
+        stage_finish(xs, M * kv8, src, xt, mx_lds);
     }
 
     f32x4_t acc[R];
@@ -586,9 +624,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
     };
 
     auto finish = [&](int t) {
-        const int mat = t >= a.tiles_per_mat ? 1 : 0;
-        void *ym = mat ? a.y1 : a.y0;
-        const int row0 = (t - mat * a.tiles_per_mat) * rows_t + grp * ROWS_W;
+        const int row0 = t * rows_t + grp * ROWS_W;
         float s[R][M];
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -603,7 +639,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
                     if (row < a.N) {
 #pragma unroll
                         for (int m = 0; m < M; ++m)
-                            store_out(a, ym, (size_t)m * a.N + row, s[r][m]);
+                            store_out(a, ym, (size_t)m * a.ldy + row, s[r][m]);
                     }
                 }
             }
@@ -628,7 +664,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 #pragma unroll
                             for (int q = 1; q < KW; ++q)
                                 v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
-                            store_out(a, ym, (size_t)m * a.N + row, v);
+                            store_out(a, ym, (size_t)m * a.ldy + row, v);
                         }
                     }
                 }
@@ -656,7 +692,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
                 finish(tile);
             tile = t2;
             b = b2;
-            return tile < a.total_tiles;
+            return tile < a.tiles;
         };
         while (run_step(wa, wb) && run_step(wb, wa)) {
         }
@@ -667,7 +703,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
                 finish(tile);
                 b = 0;
                 tile += step;
-                if (tile >= a.total_tiles)
+                if (tile >= a.tiles)
                     break;
             }
             issue(tile, b, wa);
@@ -681,15 +717,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 // float32 fused multiply-add on exactly widened bfloat16 values.
 // ---------------------------------------------------------------------------
 template <int M>
-__global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
+__global__ __launch_bounds__(256) void scalar_kernel(Args a)
 {
     const int lane = threadIdx.x & 63;
     const long long g = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (g >= (long long)nmats * a.N)
+    if (g >= (long long)a.nmats * a.N)
         return;  // whole wave
     const int mat = g >= a.N ? 1 : 0;
     const int row = (int)(g - (long long)mat * a.N);
     const uint16_t *w = (mat ? a.w1 : a.w0) + (size_t)row * a.K;
+    const uint16_t *xm = mat ? a.x1 : a.x;
     void *ym = mat ? a.y1 : a.y0;
 
     float acc[M];
@@ -700,7 +737,7 @@ __global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
         const float wf = bf16_to_f32(w[k]);
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            acc[m] = __builtin_fmaf(bf16_to_f32(a.x[(size_t)m * a.K + k]), wf, acc[m]);
+            acc[m] = __builtin_fmaf(bf16_to_f32(xm[(size_t)m * a.ldx + k]), wf, acc[m]);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m)
@@ -708,23 +745,27 @@ __global__ __launch_bounds__(256) void scalar_kernel(Args a, int nmats)
     if (lane == sum_lane<64>()) {
 #pragma unroll
         for (int m = 0; m < M; ++m)
-            store_out(a, ym, (size_t)m * a.N + row, acc[m]);
+            store_out(a, ym, (size_t)m * a.ldy + row, acc[m]);
     }
 }
 
-// K == 0: the empty sum, +0 everywhere; `count` elements of `elem_bytes` (2 or 4) each.
-__global__ __launch_bounds__(256) void zero_kernel(void *y0, void *y1, long long count, int elem_bytes)
+// K == 0: the empty sum, +0 for every (m, n) of y0 (and y1), rows at stride ldy;
+// elements of `elem_bytes` (2 or 4) bytes.
+__global__ __launch_bounds__(256) void zero_kernel(void *y0, void *y1, int N, int ldy, long long count,
+                                                   int elem_bytes)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i < count) {
+        const long long m = i / N;
+        const size_t o = (size_t)(m * ldy + (i - m * N));
         if (elem_bytes == 4) {
-            static_cast<float *>(y0)[i] = 0.0f;
+            static_cast<float *>(y0)[o] = 0.0f;
             if (y1)
-                static_cast<float *>(y1)[i] = 0.0f;
+                static_cast<float *>(y1)[o] = 0.0f;
         } else {
-            static_cast<uint16_t *>(y0)[i] = 0;
+            static_cast<uint16_t *>(y0)[o] = 0;
             if (y1)
-                static_cast<uint16_t *>(y1)[i] = 0;
+                static_cast<uint16_t *>(y1)[o] = 0;
         }
     }
 }

@@ -306,11 +306,38 @@ bool overlaps(const void *a, size_t la, const void *b, size_t lb)
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 struct Call {
-    const void *x, *w0, *w1;
+    const void *x, *x1;  // x of W0 and of W1 (x1 == x for the shared-input pair)
+    const void *w0, *w1;
     void *y0, *y1;
     int M, N, K, nmats;
-    int out_f32;  // 1: float32 outputs, 0: bfloat16
+    int ldx, ldy;        // row strides of x/x1 and y0/y1, in elements
+    int out_f32;         // 1: float32 outputs, 0: bfloat16
 };
+
+Call single_call(const void *x, const void *W, void *y, int M, int N, int K, int out_f32)
+{
+    return Call{x, x, W, nullptr, y, nullptr, M, N, K, 1, K, N, out_f32};
+}
+
+// Bytes spanned by `rows` rows of `width` elements at `stride` elements.
+size_t span(int rows, int width, int stride, size_t elem)
+{
+    return rows > 0 && width > 0 ? ((size_t)(rows - 1) * stride + width) * elem : 0;
+}
+
+// Two same-shape row-strided blocks (rows x width at the same stride, in bytes)
+// share no byte. Exact when the strides are equal: the second block's rows must
+// fall in the gaps between the first block's rows, or the spans must not meet.
+bool strided_disjoint(const void *p, const void *q, int rows, size_t width, size_t stride)
+{
+    const size_t s = (size_t)(rows - 1) * stride + width;
+    if (!overlaps(p, s, q, s))
+        return true;
+    const long long d = (long long)(reinterpret_cast<uintptr_t>(q) - reinterpret_cast<uintptr_t>(p));
+    const long long st = (long long)stride;
+    const long long r = ((d % st) + st) % st;  // q's rows start r bytes into p's stride period
+    return r >= (long long)width && r + (long long)width <= st;
+}
 
 int validate(const Call &c)
 {
@@ -318,34 +345,40 @@ int validate(const Call &c)
         return SKINNY_ERR_INVALID_ARG;
     if (c.M == 0 || c.N == 0)
         return SKINNY_OK;
+    if (c.ldx < c.K || c.ldy < c.N)
+        return SKINNY_ERR_INVALID_ARG;
     if (!c.y0 || (c.nmats == 2 && !c.y1))
         return SKINNY_ERR_INVALID_ARG;
-    if (c.K > 0 && (!c.x || !c.w0 || (c.nmats == 2 && !c.w1)))
+    if (c.K > 0 && (!c.x || !c.w0 || (c.nmats == 2 && (!c.w1 || !c.x1))))
         return SKINNY_ERR_INVALID_ARG;
-    const void *ptrs[5] = {c.x, c.w0, c.nmats == 2 ? c.w1 : nullptr, c.y0, c.nmats == 2 ? c.y1 : nullptr};
+    const void *ptrs[6] = {c.x, c.nmats == 2 ? c.x1 : nullptr, c.w0, c.nmats == 2 ? c.w1 : nullptr,
+                           c.y0, c.nmats == 2 ? c.y1 : nullptr};
     for (const void *p : ptrs)
         if (p && !aligned(p, 2))
             return SKINNY_ERR_INVALID_ARG;
     const size_t ye = c.out_f32 ? 4 : 2;
     if (c.out_f32 && (!aligned(c.y0, 4) || (c.nmats == 2 && !aligned(c.y1, 4))))
         return SKINNY_ERR_INVALID_ARG;
-    const size_t xb = (size_t)c.M * c.K * 2, wb = (size_t)c.N * c.K * 2, yb = (size_t)c.M * c.N * ye;
+    const size_t xb = span(c.M, c.K, c.ldx, 2), wb = (size_t)c.N * c.K * 2;
+    const size_t yb = span(c.M, c.N, c.ldy, ye);
     for (int i = 0; i < c.nmats; ++i) {
         void *y = i ? c.y1 : c.y0;
         if (overlaps(y, yb, c.x, xb) || overlaps(y, yb, c.w0, wb) ||
-            (c.nmats == 2 && overlaps(y, yb, c.w1, wb)))
+            (c.nmats == 2 && (overlaps(y, yb, c.w1, wb) || overlaps(y, yb, c.x1, xb))))
             return SKINNY_ERR_INVALID_ARG;
     }
-    if (c.nmats == 2 && overlaps(c.y0, yb, c.y1, yb))
+    if (c.nmats == 2 && !strided_disjoint(c.y0, c.y1, c.M, (size_t)c.N * ye, (size_t)c.ldy * ye))
         return SKINNY_ERR_INVALID_ARG;
     return SKINNY_OK;
 }
 
-// 128-bit weight loads need 16-byte aligned rows; buffer offsets are 32-bit.
+// 128-bit loads need 16-byte aligned rows of x and W; buffer offsets are 32-bit.
 bool vector_ok(const Call &c)
 {
-    const bool al = aligned(c.x, 16) && aligned(c.w0, 16) && (c.nmats == 1 || aligned(c.w1, 16));
-    return al && c.K % 8 == 0 && c.K <= (1 << 20);
+    const bool al = aligned(c.x, 16) && aligned(c.w0, 16) &&
+                    (c.nmats == 1 || (aligned(c.w1, 16) && aligned(c.x1, 16)));
+    return al && c.K % 8 == 0 && c.ldx % 8 == 0 && c.K <= (1 << 20) &&
+           span(c.M, c.K, c.ldx, 2) < (1u << 31);
 }
 
 // The MFMA family needs whole batches of 128 * chunks in every k_split slice.
@@ -460,8 +493,9 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         long long count = (long long)c.M * c.N;
         void *y0 = c.y0;
         void *y1 = c.nmats == 2 ? c.y1 : nullptr;
+        int n = c.N, ldy = c.ldy;
         int elem = c.out_f32 ? 4 : 2;
-        void *args[] = {&y0, &y1, &count, &elem};
+        void *args[] = {&y0, &y1, &n, &ldy, &count, &elem};
         const long long blocks = (count + 255) / 256;
         if (blocks > 0x7FFFFFFF)
             return SKINNY_ERR_INVALID_ARG;
@@ -496,41 +530,38 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
 
     skg::Args a{};
     a.x = static_cast<const uint16_t *>(c.x);
+    a.x1 = static_cast<const uint16_t *>(c.nmats == 2 ? c.x1 : c.x);
     a.w0 = static_cast<const uint16_t *>(c.w0);
     a.w1 = static_cast<const uint16_t *>(c.nmats == 2 ? c.w1 : c.w0);
     a.y0 = c.y0;
     a.y1 = c.nmats == 2 ? c.y1 : c.y0;
     a.N = c.N;
     a.K = c.K;
+    a.ldx = c.ldx;
+    a.ldy = c.ldy;
+    a.nmats = c.nmats;
     a.out_f32 = c.out_f32;
 
     const int vidx = (int)(v - kAllVariants);
     hipError_t err;
+    auto launch_scalar = [&]() {
+        const long long blocks = ((long long)c.nmats * c.N + 3) / 4;  // one wave per output row
+        a.tiles = 0;
+        void *args[] = {&a};
+        return launch(registry().scalar->fn[c.M - 1], (int)blocks, 256, 0, args, stream);
+    };
     if (plan.kind == SKINNY_KIND_SCALAR) {
-        int nmats = c.nmats;
-        const long long rows = (long long)c.nmats * c.N;
-        const long long blocks = (rows + 3) / 4;
-        if (blocks > 0x7FFFFFFF)
-            return SKINNY_ERR_INVALID_ARG;
-        a.tiles_per_mat = 0;
-        a.total_tiles = 0;
-        void *args[] = {&a, &nmats};
-        err = launch(v->fn[c.M - 1], (int)blocks, 256, 0, args, stream);
+        err = launch_scalar();
     } else {
         const int waves = plan.threads_per_block / 64;
         const long long rows_per_tile = (long long)(waves / plan.k_split) * v->rows_per_group;
         const long long tiles = ((long long)c.N + rows_per_tile - 1) / rows_per_tile;
-        const long long total = tiles * c.nmats;
-        if (total > (1LL << 30))  // keeps tile + gridDim.x inside int in the kernels
+        if (tiles > (1LL << 30))  // keeps tile + step inside int in the kernels
             return SKINNY_ERR_INVALID_ARG;
         // every buffer resource spans at most one wave group's rows
         if ((long long)v->rows_per_group * c.K * 2 > 0x7FFFFFFFLL)
             return plan_in ? SKINNY_ERR_INVALID_ARG : SKINNY_ERR_UNSUPPORTED;
-        a.tiles_per_mat = (int)tiles;
-        a.total_tiles = (int)total;
-        int grid = (int)total;
-        if (plan.grid_blocks > 0 && plan.grid_blocks < grid)
-            grid = plan.grid_blocks;
+        a.tiles = (int)tiles;
         // Dynamic LDS: x staged as [M][Kpad] (LOOP_K) or [M][K] (MFMA).
         int kpad = c.K;
         size_t lds = 0;
@@ -542,19 +573,14 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
             lds = (size_t)c.M * c.K * 2;
         }
         const void *fn = v->fn[c.M - 1];
-        int block = plan.threads_per_block;
+        const int block = plan.threads_per_block;
         const int st_lds = lds > 0 ? static_lds(vidx, c.M, fn) : 0;
         if (st_lds < 0)
             return SKINNY_ERR_LAUNCH;
         if (lds + (size_t)st_lds > (size_t)dev.max_lds) {
             if (plan_in)
                 return SKINNY_ERR_UNSUPPORTED;
-            // x does not fit in LDS: element-wise path
-            fn = registry().scalar->fn[c.M - 1];
-            const long long blocks = ((long long)c.nmats * c.N + 3) / 4;
-            int nmats = c.nmats;
-            void *args[] = {&a, &nmats};
-            err = launch(fn, (int)blocks, 256, 0, args, stream);
+            err = launch_scalar();  // x does not fit in LDS: element-wise path
             return err == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
         }
         if (lds > 65536 && !g_lds_raised[vidx][c.M - 1].load(std::memory_order_acquire)) {
@@ -566,13 +592,15 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
             }
             g_lds_raised[vidx][c.M - 1].store(1, std::memory_order_release);
         }
-        // Default: a persistent grid that fills the device once, so every wave
-        // loads x once and then streams many rows.
-        if (plan.grid_blocks == 0) {
-            const long long cap = (long long)dev.cus * blocks_per_cu(vidx, c.M, fn, block, lds);
-            if (cap < grid)
-                grid = (int)cap;
-        }
+        // Blocks per weight: one per tile, or a persistent grid that fills the device
+        // once (grid_blocks == 0), or at most grid_blocks; a pair launches the same
+        // count for each weight (even blocks W0, odd blocks W1).
+        long long cap = plan.grid_blocks > 0
+                            ? plan.grid_blocks
+                            : (long long)dev.cus * blocks_per_cu(vidx, c.M, fn, block, lds);
+        cap = (cap + c.nmats - 1) / c.nmats;
+        const long long per = tiles < cap ? tiles : (cap > 0 ? cap : 1);
+        const int grid = (int)(per * c.nmats);
         if (plan.kind == SKINNY_KIND_LOOP_K) {
             void *args[] = {&a, &kpad};
             err = launch(fn, grid, block, lds, args, stream);
@@ -592,15 +620,13 @@ int skinny_gemm_init(int device) { return check_device(device, nullptr); }
 
 int skinny_gemm_bf16(const void *x, const void *W, void *y, int M, int N, int K, hipStream_t stream)
 {
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 0}, nullptr, stream);
+    return run(single_call(x, W, y, M, N, K, 0), nullptr, stream);
 }
 
 int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1, void *y0, void *y1, int M,
                           int N, int K, hipStream_t stream)
 {
-    if (!W1 && K > 0 && M > 0 && N > 0)
-        return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W0, W1, y0, y1, M, N, K, 2, 0}, nullptr, stream);
+    return run(Call{x, x, W0, W1, y0, y1, M, N, K, 2, K, N, 0}, nullptr, stream);
 }
 
 int skinny_gemm_bf16_ex(const void *x, const void *W, void *y, int M, int N, int K,
@@ -608,7 +634,7 @@ int skinny_gemm_bf16_ex(const void *x, const void *W, void *y, int M, int N, int
 {
     if (!plan)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 0}, plan, stream);
+    return run(single_call(x, W, y, M, N, K, 0), plan, stream);
 }
 
 int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1, void *y0, void *y1,
@@ -616,13 +642,29 @@ int skinny_gemm_bf16_pair_ex(const void *x, const void *W0, const void *W1, void
 {
     if (!plan)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W0, W1, y0, y1, M, N, K, 2, 0}, plan, stream);
+    return run(Call{x, x, W0, W1, y0, y1, M, N, K, 2, K, N, 0}, plan, stream);
+}
+
+int skinny_gemm_bf16_pair_strided(const void *x0, const void *x1, int ldx, const void *W0,
+                                  const void *W1, void *y0, void *y1, int ldy, int M, int N, int K,
+                                  hipStream_t stream)
+{
+    return run(Call{x0, x1, W0, W1, y0, y1, M, N, K, 2, ldx, ldy, 0}, nullptr, stream);
+}
+
+int skinny_gemm_bf16_pair_strided_ex(const void *x0, const void *x1, int ldx, const void *W0,
+                                     const void *W1, void *y0, void *y1, int ldy, int M, int N,
+                                     int K, const skinny_plan_t *plan, hipStream_t stream)
+{
+    if (!plan)
+        return SKINNY_ERR_INVALID_ARG;
+    return run(Call{x0, x1, W0, W1, y0, y1, M, N, K, 2, ldx, ldy, 0}, plan, stream);
 }
 
 int skinny_gemm_bf16_f32out(const void *x, const void *W, float *y, int M, int N, int K,
                             hipStream_t stream)
 {
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 1}, nullptr, stream);
+    return run(single_call(x, W, y, M, N, K, 1), nullptr, stream);
 }
 
 int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y, int M, int N, int K,
@@ -630,7 +672,7 @@ int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y, int M, in
 {
     if (!plan)
         return SKINNY_ERR_INVALID_ARG;
-    return run(Call{x, W, nullptr, y, nullptr, M, N, K, 1, 1}, plan, stream);
+    return run(single_call(x, W, y, M, N, K, 1), plan, stream);
 }
 
 int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out)

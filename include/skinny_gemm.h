@@ -123,6 +123,29 @@ int skinny_gemm_bf16(const void *x, const void *W, void *y,
 int skinny_gemm_bf16_pair(const void *x, const void *W0, const void *W1,
                           void *y0, void *y1, int M, int N, int K, hipStream_t stream);
 
+/* The paired projection in the form the f_b_proj / g_b_proj pair actually takes:
+ * each weight has its own input, two row-strided views of one merged activation
+ * (vLLM PR #57617, paired KDA gate projections, section "Controlled follow-up": a
+ * narrow -> unflatten -> transpose view over the merged f_a/g_a output feeding one
+ * batched matmul; LMDeploy PR #4968, section Optimizations: f_a/g_a merged, f_b/g_b
+ * batched). y0 = x0 . W0^T and y1 = x1 . W1^T in ONE launch, where row m of x0 is
+ * the K elements at x0 + m*ldx, likewise x1, and row m of y0 / y1 is the N
+ * elements at y0 + m*ldy / y1 + m*ldy. Typical use: a merged [M][2K] activation
+ * with x0 = base, x1 = base + K, ldx = 2K, and a merged [M][2N] output with
+ * y1 = y0 + N, ldy = 2N. ldx >= K and ldy >= N (else SKINNY_ERR_INVALID_ARG);
+ * x0/x1 may overlap each other (they are only read); y0 and y1 must share no
+ * element with each other, x0, x1, W0 or W1. The fast path needs x0, x1, W0, W1
+ * 16-byte aligned and ldx % 8 == 0. Other conventions as skinny_gemm_bf16_pair. */
+int skinny_gemm_bf16_pair_strided(const void *x0, const void *x1, int ldx,
+                                  const void *W0, const void *W1,
+                                  void *y0, void *y1, int ldy,
+                                  int M, int N, int K, hipStream_t stream);
+int skinny_gemm_bf16_pair_strided_ex(const void *x0, const void *x1, int ldx,
+                                     const void *W0, const void *W1,
+                                     void *y0, void *y1, int ldy,
+                                     int M, int N, int K, const skinny_plan_t *plan,
+                                     hipStream_t stream);
+
 /* As skinny_gemm_bf16 / _pair, with an explicit plan (used by the plan sweep
  * and by tests). The plan must name a compiled variant (see
  * skinny_gemm_num_variants) compatible with K: for FIXED_K, K must equal

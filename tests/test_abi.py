@@ -248,3 +248,27 @@ def test_no_device(skg):
     assert st in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
     assert L.skinny_gemm_init(0) in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
     assert L.skinny_gemm_init(-1) == skg.SKINNY_ERR_INVALID_ARG
+
+
+def test_pair_strided_validation(skg):
+    """Strides below the row length and outputs that share elements are rejected
+    before any device work; outputs interleaved in one merged tensor are valid (on a
+    machine without a GPU such a call gets past validation and stops at the device
+    check)."""
+    L = skg.lib()
+    M, N, K = 2, 16, 32
+    x0, x1 = X, X + 2 * K
+    y0 = Y
+    bad = [
+        (x0, x1, K - 1, W, W1, y0, Y1, N, M, N, K),          # ldx < K
+        (x0, x1, 2 * K, W, W1, y0, Y1, N - 1, M, N, K),      # ldy < N
+        (x0, x1, 2 * K, W, W1, y0, y0 + 2, 2 * N, M, N, K),  # y1 overlaps y0's rows
+        (x0, x1, 2 * K, W, W1, y0, x1 + 4, N, M, N, K),      # y1 overlaps x1
+        (x0, None, 2 * K, W, W1, y0, Y1, N, M, N, K),        # null x1
+    ]
+    for b in bad:
+        assert L.skinny_gemm_bf16_pair_strided(*b, None) == skg.SKINNY_ERR_INVALID_ARG, b
+    # merged output [M][2N]: y1 = y0 + N elements, ldy = 2N -> disjoint, accepted
+    ok = (x0, x1, 2 * K, W, W1, y0, y0 + 2 * N, 2 * N, M, N, K)
+    if not __import__("torch").cuda.is_available():
+        assert L.skinny_gemm_bf16_pair_strided(*ok, None) == skg.SKINNY_ERR_UNSUPPORTED

@@ -553,3 +553,82 @@ def test_f32_output_rejects_misaligned(skg):
     assert st == skg.SKINNY_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(buf == 0)
+
+
+# ---------------------------------------------------------------------------
+# strided paired form: two halves of a merged activation, merged output
+# ---------------------------------------------------------------------------
+
+def _merged_case(M, N, K, seed, extra_cols=0):
+    xm = synth.activations(M, 2 * K + extra_cols, seed=seed, shape_id=K, tensor_id=0)
+    W0 = synth.weights(N, K, seed=seed, shape_id=K, tensor_id=1)
+    W1 = synth.weights(N, K, seed=seed, shape_id=K, tensor_id=2)
+    return xm, W0, W1
+
+
+@pytest.mark.parametrize("N,K", [(4096, 128), (2048, 128), (300, 1024), (129, 1536)])
+def test_pair_strided_merged(skg, N, K):
+    for M in (1, 2, 3, 4):
+        xm, W0, W1 = _merged_case(M, N, K, seed=100 + M)
+        xmd = to_dev(xm)
+        W0d, W1d = to_dev(W0), to_dev(W1)
+        y0, y1 = skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], W0d, W1d)
+        torch.cuda.synchronize()
+        x0 = np.ascontiguousarray(xm[:, :K])
+        x1 = np.ascontiguousarray(xm[:, K:])
+        check(y0.contiguous(), x0, W0, label=f"strided y0 M={M} N={N} K={K}")
+        check(y1.contiguous(), x1, W1, label=f"strided y1 M={M} N={N} K={K}")
+        # identical bits to two single calls with the same plan on contiguous inputs
+        plan, _ = skg.skinny_gemm_get_plan(N, K, M)
+        s0 = skg.gemm(to_dev(x0), W0d, plan=plan)
+        s1 = skg.gemm(to_dev(x1), W1d, plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.contiguous().view(torch.int16), s0.view(torch.int16))
+        assert torch.equal(y1.contiguous().view(torch.int16), s1.view(torch.int16))
+
+
+def test_pair_strided_every_variant(skg):
+    M = 3
+    for p in skg.variants():
+        K = variant_K(p)[0]
+        N = 2 * rows_per_tile(p) + 5
+        xm, W0, W1 = _merged_case(M, N, K, seed=110)
+        xmd = to_dev(xm)
+        try:
+            y0, y1 = skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], to_dev(W0), to_dev(W1), plan=p)
+        except skg.SkinnyError as e:
+            assert e.status == skg.SKINNY_ERR_UNSUPPORTED, str(e)
+            continue
+        torch.cuda.synchronize()
+        check(y0.contiguous(), np.ascontiguousarray(xm[:, :K]), W0, label=f"strided y0 {p}")
+        check(y1.contiguous(), np.ascontiguousarray(xm[:, K:]), W1, label=f"strided y1 {p}")
+
+
+def test_pair_strided_odd_stride_and_guard(skg):
+    """A row stride that breaks 16-byte alignment (element-wise path), separate
+    outputs, and a merged output whose gap columns must stay untouched."""
+    M, N, K = 4, 333, 128
+    xm, W0, W1 = _merged_case(M, N, K, seed=120, extra_cols=1)  # ldx = 2K + 1
+    xmd = to_dev(xm)
+    y0, y1 = skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:2 * K], to_dev(W0), to_dev(W1))
+    torch.cuda.synchronize()
+    check(y0.contiguous(), np.ascontiguousarray(xm[:, :K]), W0, label="odd stride y0")
+    check(y1.contiguous(), np.ascontiguousarray(xm[:, K:2 * K]), W1, label="odd stride y1")
+    # merged output with a guard column block between and after the halves
+    xm, W0, W1 = _merged_case(M, N, K, seed=121)
+    xmd = to_dev(xm)
+    big = torch.full((M, 3 * N + 7), -3.0, dtype=torch.bfloat16, device="cuda")
+    o0, o1 = big[:, :N], big[:, N + 7:2 * N + 7]
+    skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], to_dev(W0), to_dev(W1), out0=o0, out1=o1)
+    torch.cuda.synchronize()
+    assert torch.all(big[:, N:N + 7] == -3.0) and torch.all(big[:, 2 * N + 7:] == -3.0)
+    check(o0.contiguous(), np.ascontiguousarray(xm[:, :K]), W0, label="guard y0")
+    check(o1.contiguous(), np.ascontiguousarray(xm[:, K:]), W1, label="guard y1")
+    # K == 0 into strided outputs: zeros in the N columns only
+    e = torch.empty((M, 0), dtype=torch.bfloat16, device="cuda")
+    ew = torch.empty((N, 0), dtype=torch.bfloat16, device="cuda")
+    big.fill_(-3.0)
+    skg.gemm_pair_strided(e, e, ew, ew, out0=o0, out1=o1)
+    torch.cuda.synchronize()
+    assert torch.all(o0.view(torch.int16) == 0) and torch.all(o1.view(torch.int16) == 0)
+    assert torch.all(big[:, N:N + 7] == -3.0) and torch.all(big[:, 2 * N + 7:] == -3.0)
