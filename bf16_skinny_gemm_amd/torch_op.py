@@ -1,0 +1,105 @@
+"""PyTorch operator and module hook for the skinny GEMM.
+
+The routing follows the plan-table hook of vLLM PR #62949 (SM121 skinny GEMM
+plans, sections Claims and Details) and vLLM PR #65306 (SM90 skinny GEMM plans,
+section Details): a linear layer's apply path takes the skinny GEMM when the GPU
+architecture, the dtype and the token count qualify, and keeps the standard
+linear path otherwise. Here:
+
+* ``torch.ops.skinny.linear(x, weight)`` is a custom op (graph-capturable, with a
+  fake implementation for tracing) that always runs the HIP kernel and raises if
+  the call does not qualify;
+* :func:`skinny_linear` routes: qualifying calls go to the op, others to
+  ``torch.nn.functional.linear`` only when ``fallback=True`` (the default for the
+  module hook), else they raise;
+* :func:`install` swaps the forward of ``nn.Linear`` modules for the routed one.
+
+A call qualifies when x and weight are bfloat16 CUDA tensors on a gfx950 device,
+weight is [N, K] contiguous, x is [..., K] with 1 <= prod(leading dims) <= 4
+(the decode token count M), and there is no bias. The kernel itself never falls
+back: a missing library or a refused launch raises.
+"""
+from __future__ import annotations
+
+import functools
+
+import torch
+
+from . import gemm, lib
+
+_ARCH_OK: dict[int, bool] = {}
+
+
+def _device_is_gfx950(device: torch.device) -> bool:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _ARCH_OK:
+        props = torch.cuda.get_device_properties(idx)
+        _ARCH_OK[idx] = str(getattr(props, "gcnArchName", "")).startswith("gfx950")
+    return _ARCH_OK[idx]
+
+
+def qualifies(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None) -> bool:
+    """True when (x, weight, bias) can run on the skinny GEMM."""
+    if bias is not None:
+        return False
+    if x.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        return False
+    if x.device.type != "cuda" or weight.device != x.device:
+        return False
+    if weight.dim() != 2 or x.dim() < 1 or x.shape[-1] != weight.shape[1]:
+        return False
+    m = 1
+    for d in x.shape[:-1]:
+        m *= d
+    if not (1 <= m <= 4):
+        return False
+    return _device_is_gfx950(x.device)
+
+
+@torch.library.custom_op("skinny::linear", mutates_args=())
+def linear(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
+    """y = x @ weight.T on the HIP skinny GEMM; x [..., K] with M = prod(...) <= 4."""
+    if not qualifies(x, weight):
+        raise ValueError("skinny::linear: inputs do not qualify (bf16 on gfx950, no bias, "
+                         f"M in 1..4): x {tuple(x.shape)} {x.dtype}, weight "
+                         f"{tuple(weight.shape)} {weight.dtype}")
+    lib()  # raises if the HIP library is missing
+    lead = x.shape[:-1]
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K).contiguous()
+    w = weight.contiguous()
+    y = gemm(x2, w)
+    return y.reshape(*lead, w.shape[0])
+
+
+@linear.register_fake
+def _linear_fake(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
+    return x.new_empty((*x.shape[:-1], weight.shape[0]))
+
+
+def skinny_linear(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                  fallback: bool = True) -> torch.Tensor:
+    """F.linear semantics, routed: the skinny GEMM when the call qualifies,
+    otherwise torch.nn.functional.linear if ``fallback`` (else ValueError)."""
+    if qualifies(x, weight, bias):
+        return torch.ops.skinny.linear(x, weight)
+    if not fallback:
+        raise ValueError("skinny_linear: call does not qualify for the skinny GEMM")
+    return torch.nn.functional.linear(x, weight, bias)
+
+
+def install(module: torch.nn.Module, fallback: bool = True) -> int:
+    """Route the forward of every nn.Linear inside ``module`` through
+    :func:`skinny_linear`. Returns the number of layers hooked."""
+    count = 0
+    for sub in module.modules():
+        if isinstance(sub, torch.nn.Linear) and not getattr(sub, "_skinny_hooked", False):
+            def fwd(self, inp, _fallback=fallback):
+                return skinny_linear(inp, self.weight, self.bias, fallback=_fallback)
+            sub.forward = functools.partial(fwd, sub)
+            sub._skinny_hooked = True
+            count += 1
+    return count
+
+
+__all__ = ["linear", "skinny_linear", "install", "qualifies"]
