@@ -139,12 +139,15 @@ def kernel_name(p, M) -> str:
     nt = "true" if p.nontemporal else "false"
     if p.kind == 1:
         xl = "true" if p.x_in_lds else "false"
-        pf = "true" if p.prefetch else "false"
         return (f"void skg::fixed_k_kernel<{M}, {p.lanes_per_row}, {p.chunks}, {p.rows_per_wave}, "
-                f"{p.k_split}, {xl}, {nt}, {pf}>(skg::Args)")
+                f"{p.k_split}, {xl}, {nt}, {p.prefetch}>(skg::Args)")
     if p.kind == 2:
         return f"void skg::loop_k_kernel<{M}, {p.chunks}, {p.rows_per_wave}, {nt}>(skg::Args, int)"
-    return f"void skg::scalar_kernel<{M}>(skg::Args, int)"
+    if p.kind == 4:
+        pf = "true" if p.prefetch else "false"
+        return (f"void skg::mfma_kernel<{M}, {p.chunks}, {p.rows_per_wave}, {p.k_split}, {nt}, "
+                f"{pf}>(skg::Args)")
+    return f"void skg::scalar_kernel<{M}>(skg::Args)"
 
 
 def main() -> int:

@@ -41,10 +41,20 @@ constexpr int kAuxNontemporal = 2;
 // A byte offset that is always outside the resource: its load returns zeros.
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// Every caller passes a wave-uniform base and size (derived from the block's
+// schedule, the tile and the wave index). A buffer resource must sit in scalar
+// registers; when the compiler cannot prove an operand uniform (a row clamp that
+// it lowers to a vector med3 is enough) it wraps every load that uses the
+// resource in a readfirstlane loop, a dozen extra instructions per 16-byte load.
+// Taking lane 0's copy of each word here makes the resource scalar once.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             kBufferFlags);
+    const unsigned long long p = (unsigned long long)base;
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)p);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(p >> 32));
+    const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+    void *ub = (void *)(((unsigned long long)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, n, kBufferFlags);
 }
 
 template <bool NT>
@@ -171,11 +181,13 @@ struct Args {
     int out_f32;         // 1: y is float32 (the sum, rounded once to float32); 0: bfloat16
 };
 
-// Which weight a block serves and which of its tiles: t = first, first + step, ...
-// For a pair, even blocks serve W0 and odd blocks W1 (the host launches an even
-// grid), so a block stages one x only.
+// Which weight a block serves and which of its tiles: tile(k) for k = first,
+// first + step, ... while tile(k) < a.tiles. For a pair, even blocks serve W0 and
+// odd blocks W1 (the host launches an even grid), so a block stages one x only.
 struct Sched {
     int mat, first, step;
+
+    __device__ __forceinline__ int tile(int k) const { return k; }
 };
 
 __device__ __forceinline__ Sched block_sched(const Args &a)
@@ -214,16 +226,22 @@ __device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, f
 // multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
 // chunk reads its piece back, which frees VGPRs at M = 3, 4).
 //
-// Each block loops over the tiles of one weight (block_sched). With PF the loop
-// is software-pipelined: the loads of the next tile are issued before the
-// current one is consumed, so a wave pays the HBM latency once rather than once
-// per tile; a prefetch past the last tile uses an empty buffer resource and
-// moves no data. Without PF each tile is loaded and then consumed, which keeps
-// one register set and suits grids of one tile per block.
+// Each block loops over the tiles of one weight (block_sched). PF selects how
+// the loop overlaps loads with arithmetic:
+//   0  each tile is loaded and then consumed (one register set; suits grids of
+//      one tile per block);
+//   1  two register sets alternate: the next tile's loads are issued before the
+//      current tile is consumed;
+//   2  rolling: one register set, and chunk j of the block's next tile is loaded
+//      into the registers of chunk j as soon as they have been multiplied, so a
+//      wave keeps R*CH loads in flight through the multiply and the reduction
+//      however long those take (they grow with M).
+// A load for a tile past the last one uses an empty buffer resource and moves
+// no data.
 // ---------------------------------------------------------------------------
 constexpr int kMaxWaves = 8;  // largest block: 512 threads
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
 struct FixedK {
     static constexpr int K = KW * LPR * 8 * CH;
     static constexpr int KSLICE = K / KW;
@@ -232,10 +250,10 @@ struct FixedK {
     static_assert(64 % LPR == 0 && LPR >= 8, "lanes per row: 8, 16, 32 or 64");
     static_assert(kMaxWaves % KW == 0, "k_split must divide the largest block");
 
-    // Issue the weight loads of tile t of weight wm for this wave's rows; a tile
-    // past the last one gets an empty buffer resource and reads zeros.
-    static __device__ __forceinline__ void issue(const Args &a, const uint16_t *wm, int t, int rows_t,
-                                                 int grp, int sub, unsigned kbase, u32x4 (&wv)[R][CH])
+    // Buffer resource over this wave group's rows of tile t of weight wm; a tile
+    // past the last one gets an empty resource, whose loads read zeros.
+    static __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Args &a, const uint16_t *wm,
+                                                                     int t, int rows_t, int grp)
     {
         const uint16_t *base = wm;
         int valid = 0;
@@ -245,16 +263,29 @@ struct FixedK {
             valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
             base = wm + (size_t)row0 * K;
         }
-        const __amdgpu_buffer_rsrc_t ws = make_rsrc(base, (unsigned)(valid * K * 2));
+        return make_rsrc(base, (unsigned)(valid * K * 2));
+    }
+
+    // Byte offset of this lane's chunk j of row r within the group's rows.
+    static __device__ __forceinline__ unsigned chunk_off(int r, int sub, unsigned kbase, int j)
+    {
+        return ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u;
+    }
+
+    // Issue all weight loads of tile t for this wave's rows.
+    static __device__ __forceinline__ void issue(const Args &a, const uint16_t *wm, int t, int rows_t,
+                                                 int grp, int sub, unsigned kbase, u32x4 (&wv)[R][CH])
+    {
+        const __amdgpu_buffer_rsrc_t ws = tile_rsrc(a, wm, t, rows_t, grp);
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int j = 0; j < CH; ++j)
-                wv[r][j] = load16<NT>(ws, ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u);
+                wv[r][j] = load16<NT>(ws, chunk_off(r, sub, kbase, j));
     }
 };
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
 __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 {
     using F = FixedK<M, LPR, CH, R, KW, XL, NT, PF>;
@@ -280,13 +311,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     const uint16_t *xm = sc.mat ? a.x1 : a.x;
     void *ym = sc.mat ? a.y1 : a.y0;
 
-    int tile = sc.first;
+    int k = sc.first;
+    int tile = sc.tile(k);
     if (tile >= a.tiles)
         return;  // whole block
 
     __shared__ u32x4 x_lds[XL ? M * K / 8 : 1];
     __shared__ float part[KW > 1 ? kMaxWaves * M * ROWS_W : 1];
-    u32x4 wa[R][CH], wb[PF ? R : 1][PF ? CH : 1];
+    u32x4 wa[R][CH], wb[PF == 1 ? R : 1][PF == 1 ? CH : 1];
     u32x4 xr[XL ? 1 : M][XL ? 1 : CH];
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(xm, x_bytes(a, M));
     const int ldx = a.ldx;
@@ -309,7 +341,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 xr[m][j] = load16<false>(xs, (unsigned)(m * ldx + (int)kbase + j * LPR * 8) * 2u);
     }
 
-    auto consume = [&](int t, const u32x4 (&wv)[R][CH]) {
+    // Multiply tile t's weights wv, reduce and store; after_chunk(j) runs once
+    // chunk j of wv is no longer needed.
+    auto consume = [&](int t, const u32x4 (&wv)[R][CH], auto &&after_chunk) {
         float acc[M][R];
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -333,6 +367,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 #pragma unroll
                 for (int r = 0; r < R; ++r)
                     acc[m][r] = dot8(wv[r][j], xv, acc[m][r]);
+                if (m == M - 1)
+                    after_chunk(j);
             }
 #pragma unroll
         for (int m = 0; m < M; ++m)
@@ -382,24 +418,46 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
         }
     };
 
-    if constexpr (PF) {
-        // Two register sets alternate: while one tile is consumed, the next is in flight.
+    auto nothing = [](int) {};
+    if constexpr (PF == 2) {
         while (true) {
-            F::issue(a, wm, tile + step, rows_t, grp, sub, kbase, wb);
-            consume(tile, wa);
-            tile += step;
+            const int next = sc.tile(k + step);
+            const __amdgpu_buffer_rsrc_t wn = F::tile_rsrc(a, wm, next, rows_t, grp);
+            consume(tile, wa, [&](int j) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    wa[r][j] = load16<NT>(wn, F::chunk_off(r, sub, kbase, j));
+                // keep these loads between chunk j's products and chunk j+1's: left
+                // alone, the scheduler sinks all of them below the last chunk
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            k += step;
+            tile = next;
             if (tile >= a.tiles)
                 break;
-            F::issue(a, wm, tile + step, rows_t, grp, sub, kbase, wa);
-            consume(tile, wb);
-            tile += step;
+        }
+    } else if constexpr (PF == 1) {
+        while (true) {
+            int next = sc.tile(k + step);
+            F::issue(a, wm, next, rows_t, grp, sub, kbase, wb);
+            consume(tile, wa, nothing);
+            k += step;
+            tile = next;
+            if (tile >= a.tiles)
+                break;
+            next = sc.tile(k + step);
+            F::issue(a, wm, next, rows_t, grp, sub, kbase, wa);
+            consume(tile, wb, nothing);
+            k += step;
+            tile = next;
             if (tile >= a.tiles)
                 break;
         }
     } else {
         while (true) {
-            consume(tile, wa);
-            tile += step;
+            consume(tile, wa, nothing);
+            k += step;
+            tile = sc.tile(k);
             if (tile >= a.tiles)
                 break;
             F::issue(a, wm, tile, rows_t, grp, sub, kbase, wa);
@@ -423,7 +481,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
     const int K = a.K;
     const int kvec = kpad / 8;
     const Sched sc = block_sched(a);
-    if (sc.first >= a.tiles)
+    if (sc.tile(sc.first) >= a.tiles)
         return;  // whole block
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
@@ -442,7 +500,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
     }
 
     const int rows_t = (int)(blockDim.x >> 6) * R;
-    for (int t = sc.first; t < a.tiles; t += sc.step) {
+    for (int k = sc.first, t = sc.tile(k); t < a.tiles; k += sc.step, t = sc.tile(k)) {
         const int row0 = t * rows_t + wave * R;
         int valid = a.N - row0;
         valid = valid < 0 ? 0 : (valid > R ? R : valid);
@@ -555,7 +613,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
 
-    int tile = sc.first;
+    int k = sc.first;
+    int tile = sc.tile(k);
     if (tile >= a.tiles)
         return;  // whole block
 
@@ -681,16 +740,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
         // One step: load the next batch into `nxt`, multiply `cur`, close the tile
         // after its last batch. Returns false when no step follows.
         auto run_step = [&](const u32x4 (&cur)[R][U], u32x4 (&nxt)[R][U]) {
-            int t2 = tile, b2 = b + 1;
+            int t2 = tile, b2 = b + 1, k2 = k;
             if (b2 == nb) {
                 b2 = 0;
-                t2 = tile + step;
+                k2 = k + step;
+                t2 = sc.tile(k2);
             }
             issue(t2, b2, nxt);
             multiply(b, cur);
             if (b + 1 == nb)
                 finish(tile);
             tile = t2;
+            k = k2;
             b = b2;
             return tile < a.tiles;
         };
@@ -702,7 +763,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
             if (++b == nb) {
                 finish(tile);
                 b = 0;
-                tile += step;
+                k += step;
+                tile = sc.tile(k);
                 if (tile >= a.tiles)
                     break;
             }

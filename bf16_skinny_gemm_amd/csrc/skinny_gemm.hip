@@ -33,14 +33,14 @@ struct Variant {
 
 // Register budget per lane, so that no instance spills: x in registers takes
 // 4*M*CH VGPRs (at most 128), the weight sets in flight 4*R*CH each (two with
-// prefetch).
-constexpr bool fits(int M, int CH, int R, bool XL, bool PF)
+// tile prefetch, one without or with rolling prefetch).
+constexpr bool fits(int M, int CH, int R, bool XL, int PF)
 {
-    const int w = (PF ? 2 : 1) * R * CH;
+    const int w = (PF == 1 ? 2 : 1) * R * CH;
     return XL ? w <= 20 : (M * CH <= 32 && M * CH + w <= 48);
 }
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
+template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
 constexpr const void *fixed_fn()
 {
     if constexpr (fits(M, CH, R, XL, PF))
@@ -49,12 +49,11 @@ constexpr const void *fixed_fn()
         return nullptr;
 }
 
-template <int LPR, int CH, int R, int KW, bool XL, bool NT, bool PF>
+template <int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
 Variant fixed_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0,
-                           PF ? 1 : 0};
+    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0, PF};
     v.fn[0] = fixed_fn<1, LPR, CH, R, KW, XL, NT, PF>();
     v.fn[1] = fixed_fn<2, LPR, CH, R, KW, XL, NT, PF>();
     v.fn[2] = fixed_fn<3, LPR, CH, R, KW, XL, NT, PF>();
@@ -107,15 +106,16 @@ Variant scalar_variant()
 }
 
 // Per (lanes_per_row, chunks, k_split): one or two rows per wave, x in registers
-// or LDS, with and without tile prefetch, all with the non-temporal hint; plus
-// the plain-cached form at one row per wave (the hint won every cell of the
-// gfx950 sweep).
+// or LDS, each prefetch mode (none, tile, rolling), all with the non-temporal
+// hint; plus the plain-cached form at one row per wave (the hint won every cell
+// of the gfx950 sweep).
 #define SKG_FIXED_XP(LPR, CH, KW, XL, PF)                                                          \
     fixed_variant<LPR, CH, 1, KW, XL, true, PF>(), fixed_variant<LPR, CH, 2, KW, XL, true, PF>()
 #define SKG_FIXED(LPR, CH, KW)                                                                      \
-    SKG_FIXED_XP(LPR, CH, KW, false, false), SKG_FIXED_XP(LPR, CH, KW, false, true),                \
-        SKG_FIXED_XP(LPR, CH, KW, true, false), SKG_FIXED_XP(LPR, CH, KW, true, true),              \
-        fixed_variant<LPR, CH, 1, KW, false, false, true>()
+    SKG_FIXED_XP(LPR, CH, KW, false, 0), SKG_FIXED_XP(LPR, CH, KW, false, 1),                       \
+        SKG_FIXED_XP(LPR, CH, KW, false, 2), SKG_FIXED_XP(LPR, CH, KW, true, 0),                    \
+        SKG_FIXED_XP(LPR, CH, KW, true, 1), SKG_FIXED_XP(LPR, CH, KW, true, 2),                     \
+        fixed_variant<LPR, CH, 1, KW, false, false, 1>()
 #define SKG_LOOP(U, R) loop_variant<U, R, false>(), loop_variant<U, R, true>()
 #define SKG_MFMA_PF(U, R, KW) mfma_variant<U, R, KW, false>(), mfma_variant<U, R, KW, true>()
 #define SKG_MFMA(U, R) SKG_MFMA_PF(U, R, 1), SKG_MFMA_PF(U, R, 2), SKG_MFMA_PF(U, R, 4), SKG_MFMA_PF(U, R, 8)
@@ -401,7 +401,7 @@ int plan_ok(const skinny_plan_t &p, const Variant *v)
         return SKINNY_ERR_INVALID_ARG;
     if (p.x_in_lds != 0 && p.x_in_lds != 1)
         return SKINNY_ERR_INVALID_ARG;
-    if (p.prefetch != 0 && p.prefetch != 1)
+    if (p.prefetch < 0 || p.prefetch > (p.kind == SKINNY_KIND_FIXED_K ? 2 : 1))
         return SKINNY_ERR_INVALID_ARG;
     return SKINNY_OK;
 }
@@ -556,7 +556,7 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         const int waves = plan.threads_per_block / 64;
         const long long rows_per_tile = (long long)(waves / plan.k_split) * v->rows_per_group;
         const long long tiles = ((long long)c.N + rows_per_tile - 1) / rows_per_tile;
-        if (tiles > (1LL << 30))  // keeps tile + step inside int in the kernels
+        if (tiles > (1LL << 30))  // keeps the tile indices the kernels compute inside int
             return SKINNY_ERR_INVALID_ARG;
         // every buffer resource spans at most one wave group's rows
         if ((long long)v->rows_per_group * c.K * 2 > 0x7FFFFFFFLL)
@@ -599,7 +599,9 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
                             ? plan.grid_blocks
                             : (long long)dev.cus * blocks_per_cu(vidx, c.M, fn, block, lds);
         cap = (cap + c.nmats - 1) / c.nmats;
-        const long long per = tiles < cap ? tiles : (cap > 0 ? cap : 1);
+        if (cap < 1)
+            cap = 1;
+        const long long per = tiles < cap ? tiles : cap;
         const int grid = (int)(per * c.nmats);
         if (plan.kind == SKINNY_KIND_LOOP_K) {
             void *args[] = {&a, &kpad};

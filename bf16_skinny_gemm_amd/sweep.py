@@ -48,7 +48,18 @@ def log(msg):
     print(f"[sweep {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def candidate_plans(skg, K, M, kinds=None):
+def parse_grids(spec: str) -> tuple:
+    """Grid modes from a comma list: 'persistent' (0: one resident wave of blocks),
+    'tile' (one block per tile) or a block count (a persistent grid of at most
+    that many blocks)."""
+    out = []
+    for g in spec.split(","):
+        g = g.strip()
+        out.append(0 if g == "persistent" else BIG_GRID if g == "tile" else int(g))
+    return tuple(out)
+
+
+def candidate_plans(skg, K, M, kinds=None, grids=(0, BIG_GRID)):
     """Every (variant, block size, grid mode) able to run (K, M)."""
     out = []
     for v in skg.variants():
@@ -64,7 +75,7 @@ def candidate_plans(skg, K, M, kinds=None):
         for tpb in (128, 256, 512):
             if (tpb // 64) % d["k_split"]:
                 continue
-            for grid in (0, BIG_GRID):
+            for grid in grids:
                 out.append(skg.Plan.from_dict({**d, "threads_per_block": tpb, "grid_blocks": grid}))
     return out
 
@@ -121,6 +132,29 @@ def done_keys(path):
     return keys
 
 
+def refine_plans(skg, path, N, K, M, pair, top, grids):
+    """The `top` fastest (variant, block size) pairs of a cell in an earlier sweep
+    file, each crossed with `grids`."""
+    recs = []
+    with open(path) as f:
+        for line in f:
+            r = json.loads(line)
+            if "plan" in r and (r["N"], r["K"], r["M"], r["pair"]) == (N, K, M, pair):
+                recs.append(r)
+    recs.sort(key=lambda r: r["us"])
+    seen, out = set(), []
+    for r in recs:
+        d = {k: v for k, v in r["plan"].items() if k != "grid_blocks"}
+        key = tuple(sorted(d.items()))
+        if key in seen:
+            continue
+        seen.add(key)
+        out.extend(skg.Plan.from_dict({**d, "grid_blocks": g}) for g in grids)
+        if len(seen) >= top:
+            break
+    return out
+
+
 def measure(args):
     import torch
 
@@ -159,7 +193,10 @@ def measure(args):
                 nbytes = (4 * N * K + 2 * M * K + 4 * M * N) if pair else (2 * N * K + 2 * M * K + 2 * M * N)
                 best = None
                 kinds = {int(k) for k in args.kinds.split(",")} if args.kinds else None
-                for plan in candidate_plans(skg, K, M, kinds):
+                grids = parse_grids(args.grids)
+                plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids) if args.refine
+                         else candidate_plans(skg, K, M, kinds, grids))
+                for plan in plans:
                     try:
                         us, lo, hi = time_plan(torch, skg, x, weights, ys, plan, pair,
                                                args.trials, args.replays)
@@ -173,6 +210,9 @@ def measure(args):
                         best = (us, plan)
                 fout.write(json.dumps({"N": N, "K": K, "M": M, "pair": pair, "complete": True}) + "\n")
                 fout.flush()
+                if best is None:
+                    log(f"  M={M}: no plan ran")
+                    continue
                 log(f"  M={M}: best {best[0]:.3f} us {nbytes / (best[0] * 1e-6) / 1e9:.0f} GB/s {best[1]}")
             del weights, base
             torch.cuda.empty_cache()
@@ -224,6 +264,11 @@ def main():
     ap.add_argument("--only", help="comma list of NxK shapes to sweep")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
     ap.add_argument("--kinds", help="comma list of plan kinds to time (default: all)")
+    ap.add_argument("--grids", default="persistent,tile",
+                    help="comma list of grid modes: persistent, tile, or a block count")
+    ap.add_argument("--refine", metavar="JSONL",
+                    help="time only the --top fastest plans per cell of this earlier sweep, at --grids")
+    ap.add_argument("--top", type=int, default=16)
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--replays", type=int, default=5)
     args = ap.parse_args()

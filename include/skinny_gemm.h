@@ -98,7 +98,10 @@ typedef struct skinny_plan {
                                   SCALAR: always 0 */
     int32_t prefetch;          /* FIXED_K, MFMA: 1 = the next tile's (MFMA: the next K batch's)
                                   weights are loaded while the current one is consumed (two
-                                  register sets); 0 = one at a time; other kinds: always 0 */
+                                  register sets); 0 = one at a time. FIXED_K also 2 = rolling:
+                                  one register set, each 16-byte chunk of the next tile is
+                                  loaded as soon as the same chunk of the current tile has been
+                                  multiplied. Other kinds: always 0 */
 } skinny_plan_t;
 
 /* Checks that `device` is a gfx950 GPU and caches its properties. Optional:
@@ -175,9 +178,11 @@ int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y,
  * the default plan, or SKINNY_ERR_INVALID_ARG. Host-only: needs no device. */
 int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out);
 
-/* Enumerates the compiled variants (grid_blocks = 0 in each). Every variant is
- * compiled for M = 1..4. skinny_gemm_get_variant returns SKINNY_OK or
- * SKINNY_ERR_INVALID_ARG for an index out of range. Host-only. */
+/* Enumerates the compiled variants (grid_blocks = 0 in each). A variant covers
+ * M = 1..4 except an M whose instance would exceed its register budget; a plan
+ * naming it at that M returns SKINNY_ERR_UNSUPPORTED. skinny_gemm_get_variant
+ * returns SKINNY_OK or SKINNY_ERR_INVALID_ARG for an index out of range.
+ * Host-only. */
 int skinny_gemm_num_variants(void);
 int skinny_gemm_get_variant(int index, skinny_plan_t *out);
 

@@ -105,32 +105,38 @@ def test_every_variant(skg, plan):
     for K in variant_K(plan):
         for M in (1, 2, 3, 4):
             tile = rows_per_tile(plan)
-            N = 3 * tile + 5
+            N = 3 * tile + 5  # four tiles, the last one ragged
             x = synth.activations(M, K, seed=0, shape_id=K, tensor_id=M)
             W = synth.weights(N, K, seed=0, shape_id=K, tensor_id=1)
             xd, Wd = to_dev(x), to_dev(W)
-            try:
-                y = skg.gemm(xd, Wd, plan=plan)
-            except skg.SkinnyError as e:
-                # this M exceeds the variant's register budget (fixed-K), or x of this
-                # K does not fit in a block's LDS (kinds that stage x there)
-                assert e.status == skg.SKINNY_ERR_UNSUPPORTED, str(e)
-                assert plan.kind == 1 or M * K * 2 > 64 * 1024, str(e)
-                continue
-            torch.cuda.synchronize()
-            check(y, x, W, label=f"{plan} M={M} N={N} K={K}")
-            ran += 1
+            # the plan's own grid (one tile per block), then one block looping over all
+            # four tiles and three blocks taking two, one and one: every prefetch mode
+            # runs its multi-tile loop, odd and even trip counts
+            for grid in (plan.grid_blocks, 1, 3):
+                q = skg.Plan.from_dict({**plan.as_dict(), "grid_blocks": grid})
+                try:
+                    y = skg.gemm(xd, Wd, plan=q)
+                except skg.SkinnyError as e:
+                    # this M exceeds the variant's register budget (fixed-K), or x of this
+                    # K does not fit in a block's LDS (kinds that stage x there)
+                    assert e.status == skg.SKINNY_ERR_UNSUPPORTED, str(e)
+                    assert plan.kind == 1 or M * K * 2 > 64 * 1024, str(e)
+                    break
+                torch.cuda.synchronize()
+                check(y, x, W, label=f"{q} M={M} N={N} K={K}")
+                ran += 1
     assert ran > 0, f"no M runs on {plan}"
 
 
 @pytest.mark.parametrize("tpb", [64, 128, 512])
 def test_block_sizes_and_persistent_grid(skg, tpb):
-    """Launch-time knobs: block size and a persistent grid smaller than the tile count."""
+    """Launch-time knobs: block size, and persistent grids smaller than the tile
+    count (6 tiles over 2 or 4 blocks: three, or two and one, tiles per block)."""
     for K in (1024, 4096):
         for p in skg.variants():
             if p.kind != 1 or fixed_k(p) != K or (tpb // 64) % p.k_split:
                 continue
-            for grid in (0, 7):
+            for grid in (0, 2, 4):
                 q = skg.Plan.from_dict({**p.as_dict(), "threads_per_block": tpb, "grid_blocks": grid})
                 M = 2
                 N = 5 * rows_per_tile(q) + 3
