@@ -181,13 +181,13 @@ struct Args {
     int out_f32;         // 1: y is float32 (the sum, rounded once to float32); 0: bfloat16
 };
 
-// Which weight a block serves and which of its tiles: tile(k) for k = first,
-// first + step, ... while tile(k) < a.tiles. For a pair, even blocks serve W0 and
+// Which weight a block serves and which of its tiles: tile(it) for it = first,
+// first + step, ... while tile(it) < a.tiles. For a pair, even blocks serve W0 and
 // odd blocks W1 (the host launches an even grid), so a block stages one x only.
 struct Sched {
     int mat, first, step;
 
-    __device__ __forceinline__ int tile(int k) const { return k; }
+    __device__ __forceinline__ int tile(int it) const { return it; }
 };
 
 __device__ __forceinline__ Sched block_sched(const Args &a)
@@ -210,6 +210,30 @@ __device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, f
         static_cast<float *>(ym)[idx] = v;
     else
         static_cast<uint16_t *>(ym)[idx] = f32_to_bf16(v);
+}
+
+// Output row m of ym (N elements) as a buffer resource: a store to a row >= N,
+// or at offset kOutOfRange, is dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const Args &a, void *ym, int m)
+{
+    const unsigned eb = a.out_f32 ? 4u : 2u;
+    return make_rsrc(static_cast<char *>(ym) + (size_t)m * a.ldy * eb, (unsigned)a.N * eb);
+}
+
+// Store v as output `row` through the row resource yr if `mine`; otherwise the
+// store is issued with an out-of-range offset and writes nothing. The storing
+// waves of the fast kernels call it from every lane, with no per-lane branch
+// around it (the row bound is the resource's), which measured 1-7% faster per
+// call than lane-predicated global stores behind such branches.
+__device__ __forceinline__ void store_row(const Args &a, __amdgpu_buffer_rsrc_t yr, int row, bool mine,
+                                          float v)
+{
+    if (a.out_f32)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), yr,
+                                              (int)(mine ? (unsigned)row * 4u : kOutOfRange), 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), yr,
+                                              (int)(mine ? (unsigned)row * 2u : kOutOfRange), 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -310,9 +334,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     const uint16_t *xm = sc.mat ? a.x1 : a.x;
     void *ym = sc.mat ? a.y1 : a.y0;
+    __amdgpu_buffer_rsrc_t yr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        yr[m] = out_rsrc(a, ym, m);
 
-    int k = sc.first;
-    int tile = sc.tile(k);
+    int it = sc.first;
+    int tile = sc.tile(it);
     if (tile >= a.tiles)
         return;  // whole block
 
@@ -378,17 +406,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 
         const int row0 = t * rows_t + grp * ROWS_W;
         if constexpr (KW == 1) {
-            if (kl == OUT) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = row0 + r * RPI + sub;
-                    if (row < a.N) {
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int m = 0; m < M; ++m)
-                            store_out(a, ym, (size_t)m * a.ldy + row, acc[m][r]);
-                    }
-                }
-            }
+                for (int m = 0; m < M; ++m)
+                    store_row(a, yr[m], row0 + r * RPI + sub, kl == OUT, acc[m][r]);
         } else {
             if (kl == OUT) {
 #pragma unroll
@@ -398,21 +420,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                         part[((grp * KW + kw) * M + m) * ROWS_W + r * RPI + sub] = acc[m][r];
             }
             __syncthreads();
-            if (kw == 0 && kl == OUT) {
+            // the group's first wave sums and stores (a wave-uniform branch: the
+            // other waves issue no stores, so nothing delays their loads)
+            if (kw == 0) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = row0 + r * RPI + sub;
-                    if (row < a.N) {
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            float s = part[((grp * KW + 0) * M + m) * ROWS_W + r * RPI + sub];
+                    for (int m = 0; m < M; ++m) {
+                        float s = part[((grp * KW + 0) * M + m) * ROWS_W + r * RPI + sub];
 #pragma unroll
-                            for (int q = 1; q < KW; ++q)
-                                s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
-                            store_out(a, ym, (size_t)m * a.ldy + row, s);
-                        }
+                        for (int q = 1; q < KW; ++q)
+                            s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
+                        store_row(a, yr[m], row0 + r * RPI + sub, kl == OUT, s);
                     }
-                }
             }
             __syncthreads();
         }
@@ -421,7 +441,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     auto nothing = [](int) {};
     if constexpr (PF == 2) {
         while (true) {
-            const int next = sc.tile(k + step);
+            const int next = sc.tile(it + step);
             const __amdgpu_buffer_rsrc_t wn = F::tile_rsrc(a, wm, next, rows_t, grp);
             consume(tile, wa, [&](int j) {
 #pragma unroll
@@ -431,24 +451,24 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 // alone, the scheduler sinks all of them below the last chunk
                 __builtin_amdgcn_sched_barrier(0);
             });
-            k += step;
+            it += step;
             tile = next;
             if (tile >= a.tiles)
                 break;
         }
     } else if constexpr (PF == 1) {
         while (true) {
-            int next = sc.tile(k + step);
+            int next = sc.tile(it + step);
             F::issue(a, wm, next, rows_t, grp, sub, kbase, wb);
             consume(tile, wa, nothing);
-            k += step;
+            it += step;
             tile = next;
             if (tile >= a.tiles)
                 break;
-            next = sc.tile(k + step);
+            next = sc.tile(it + step);
             F::issue(a, wm, next, rows_t, grp, sub, kbase, wa);
             consume(tile, wb, nothing);
-            k += step;
+            it += step;
             tile = next;
             if (tile >= a.tiles)
                 break;
@@ -456,8 +476,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     } else {
         while (true) {
             consume(tile, wa, nothing);
-            k += step;
-            tile = sc.tile(k);
+            it += step;
+            tile = sc.tile(it);
             if (tile >= a.tiles)
                 break;
             F::issue(a, wm, tile, rows_t, grp, sub, kbase, wa);
@@ -485,6 +505,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
         return;  // whole block
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
+    __amdgpu_buffer_rsrc_t yr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        yr[m] = out_rsrc(a, ym, m);
 
     {
         const __amdgpu_buffer_rsrc_t xs = make_rsrc(sc.mat ? a.x1 : a.x, x_bytes(a, M));
@@ -500,7 +524,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
     }
 
     const int rows_t = (int)(blockDim.x >> 6) * R;
-    for (int k = sc.first, t = sc.tile(k); t < a.tiles; k += sc.step, t = sc.tile(k)) {
+    for (int it = sc.first, t = sc.tile(it); t < a.tiles; it += sc.step, t = sc.tile(it)) {
         const int row0 = t * rows_t + wave * R;
         int valid = a.N - row0;
         valid = valid < 0 ? 0 : (valid > R ? R : valid);
@@ -542,17 +566,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
             for (int r = 0; r < R; ++r)
                 acc[m][r] = group_sum<64>(acc[m][r]);
 
-        if (lane == sum_lane<64>()) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int row = row0 + r;
-                if (row < a.N) {
+        for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int m = 0; m < M; ++m)
-                        store_out(a, ym, (size_t)m * a.ldy + row, acc[m][r]);
-                }
-            }
-        }
+            for (int m = 0; m < M; ++m)
+                store_row(a, yr[m], row0 + r, lane == sum_lane<64>(), acc[m][r]);
     }
 }
 
@@ -612,9 +630,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
     const int step = sc.step;
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
+    __amdgpu_buffer_rsrc_t yr[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+        yr[m] = out_rsrc(a, ym, m);
 
-    int k = sc.first;
-    int tile = sc.tile(k);
+    int it = sc.first;
+    int tile = sc.tile(it);
     if (tile >= a.tiles)
         return;  // whole block
 
@@ -691,17 +713,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
             for (int m = 0; m < M; ++m)
                 s[r][m] = block_sum(acc[r][m]);
         if constexpr (KW == 1) {
-            if (lb == 0) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int row = row0 + r * 4 + lj;
-                    if (row < a.N) {
+            for (int r = 0; r < R; ++r)
 #pragma unroll
-                        for (int m = 0; m < M; ++m)
-                            store_out(a, ym, (size_t)m * a.ldy + row, s[r][m]);
-                    }
-                }
-            }
+                for (int m = 0; m < M; ++m)
+                    store_row(a, yr[m], row0 + r * 4 + lj, lb == 0, s[r][m]);
         } else {
             if (lb == 0) {
 #pragma unroll
@@ -711,20 +727,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
                         part[((grp * KW + kw) * ROWS_W + r * 4 + lj) * M + m] = s[r][m];
             }
             __syncthreads();
-            if (kw == 0 && lb == 0) {
+            // the group's first wave sums and stores (a wave-uniform branch)
+            if (kw == 0) {
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     const int rr = r * 4 + lj;
-                    const int row = row0 + rr;
-                    if (row < a.N) {
 #pragma unroll
-                        for (int m = 0; m < M; ++m) {
-                            float v = part[((grp * KW + 0) * ROWS_W + rr) * M + m];
+                    for (int m = 0; m < M; ++m) {
+                        float v = part[((grp * KW + 0) * ROWS_W + rr) * M + m];
 #pragma unroll
-                            for (int q = 1; q < KW; ++q)
-                                v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
-                            store_out(a, ym, (size_t)m * a.ldy + row, v);
-                        }
+                        for (int q = 1; q < KW; ++q)
+                            v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
+                        store_row(a, yr[m], row0 + rr, lb == 0, v);
                     }
                 }
             }
@@ -740,18 +754,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
         // One step: load the next batch into `nxt`, multiply `cur`, close the tile
         // after its last batch. Returns false when no step follows.
         auto run_step = [&](const u32x4 (&cur)[R][U], u32x4 (&nxt)[R][U]) {
-            int t2 = tile, b2 = b + 1, k2 = k;
+            int t2 = tile, b2 = b + 1, it2 = it;
             if (b2 == nb) {
                 b2 = 0;
-                k2 = k + step;
-                t2 = sc.tile(k2);
+                it2 = it + step;
+                t2 = sc.tile(it2);
             }
             issue(t2, b2, nxt);
             multiply(b, cur);
             if (b + 1 == nb)
                 finish(tile);
             tile = t2;
-            k = k2;
+            it = it2;
             b = b2;
             return tile < a.tiles;
         };
@@ -763,8 +777,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
             if (++b == nb) {
                 finish(tile);
                 b = 0;
-                k += step;
-                tile = sc.tile(k);
+                it += step;
+                tile = sc.tile(it);
                 if (tile >= a.tiles)
                     break;
             }

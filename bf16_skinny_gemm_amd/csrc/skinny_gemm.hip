@@ -561,6 +561,13 @@ int run(const Call &c, const skinny_plan_t *plan_in, hipStream_t stream)
         // every buffer resource spans at most one wave group's rows
         if ((long long)v->rows_per_group * c.K * 2 > 0x7FFFFFFFLL)
             return plan_in ? SKINNY_ERR_INVALID_ARG : SKINNY_ERR_UNSUPPORTED;
+        // and one output row (N elements) of y
+        if ((long long)c.N * (c.out_f32 ? 4 : 2) > 0x7FFFFFFFLL) {
+            if (plan_in)
+                return SKINNY_ERR_UNSUPPORTED;
+            err = launch_scalar();
+            return err == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
+        }
         a.tiles = (int)tiles;
         // Dynamic LDS: x staged as [M][Kpad] (LOOP_K) or [M][K] (MFMA).
         int kpad = c.K;

@@ -29,9 +29,10 @@
  *    returns SKINNY_OK (pointers may then be NULL). K == 0 writes +0 to all of
  *    y (the empty sum). M > 4 is outside the method's decode range and is
  *    rejected with SKINNY_ERR_INVALID_ARG; the caller keeps its general GEMM.
- *  - Fast path: x and W 16-byte aligned and K % 8 == 0 (128-bit weight
- *    loads). Any other alignment or K runs a correct element-wise path; it is
- *    not an error.
+ *  - Fast path: x and W 16-byte aligned, K % 8 == 0 (128-bit weight loads)
+ *    and N * (output element bytes) < 2^31. Anything else runs a correct
+ *    element-wise path; it is not an error (an explicit plan that cannot run
+ *    returns SKINNY_ERR_INVALID_ARG or SKINNY_ERR_UNSUPPORTED instead).
  *  - Errors are returned, never raised or aborted: arguments are validated
  *    before anything is enqueued, and nothing is written on error. Only
  *    gfx950 devices are supported (others: SKINNY_ERR_UNSUPPORTED).
