@@ -41,6 +41,9 @@ WORKLOADS = {
             [(n, k, m) for (n, k) in ((2048, 4096), (4096, 1024), (8192, 1536), (4096, 8192))
              for m in (1, 2, 4)] + [("pair", 4096, 128, m) for m in (1, 2, 4)]),
     "lm_head": ("LM head (77440,4096) at M=1,2,4, cold cache", [(77440, 4096, m) for m in (1, 2, 4)]),
+    "kda_m5_8": ("KDA in_proj (12576,4096) + o_proj (4096,4096) at M=5..8, cold cache "
+                 "(beyond the decode range the cited plans cover)",
+                 [(n, 4096, m) for n in (12576, 4096) for m in (5, 6, 7, 8)]),
 }
 CHAIN = [(12576, 4096, 34), (4096, 4096, 34), (2048, 4096, 53), (4096, 1024, 42),
          (8192, 1536, 11), (4096, 8192, 11), (77440, 4096, 1)]
@@ -62,13 +65,18 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle sample budget")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.nn.functional.linear (the vendor BLAS path) on every "
+                         "cell under the same graph protocol (informational)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 256 MiB (PMC counter calibration)")
     return ap.parse_args()
 
 
-KERNEL_SOURCES = ("bf16_skinny_gemm_amd/csrc/kernels.hpp", "bf16_skinny_gemm_amd/csrc/skinny_gemm.hip",
-                  "bf16_skinny_gemm_amd/csrc/plans_gfx950.inc")
+KERNEL_SOURCES = tuple(f"bf16_skinny_gemm_amd/csrc/{f}" for f in (
+    "kernels.hpp", "variants.hpp", "skinny_gemm.hip", "variants_fixed_small.hip",
+    "variants_fixed_k4096.hip", "variants_fixed_k8192.hip", "variants_other.hip",
+    "plans_gfx950.inc"))
 
 
 def source_digest() -> str:
@@ -257,6 +265,34 @@ def main() -> int:
         for c in cells:
             run_cell(c)
 
+    def time_vendor(c):
+        # torch.nn.functional.linear on the same inputs and weight copies, same protocol
+        lin = torch.nn.functional.linear
+
+        def run():
+            if c["cell"][0] == "pair":
+                for (w0, w1) in c["ws"]:
+                    lin(c["x"], w0)
+                    lin(c["x"], w1)
+            else:
+                for w in c["ws"]:
+                    lin(c["x"], w)
+
+        gv = capture(run)
+        gv.replay()
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(args.trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.replays):
+                gv.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / (args.replays * c["calls"]))
+        del gv
+        return statistics.median(per)
+
     step_bytes = sum(bytes_per_call(c["cell"]) * c["calls"] for c in cells)
     step_calls = sum(c["calls"] for c in cells)
     log(f"capturing step: {step_calls} launches, {step_bytes / 1e9:.3f} GB per step")
@@ -311,6 +347,11 @@ def main() -> int:
         cell_rows.append(row)
         log(f"cell {row['cell']}: {us:.3f} us/call, {gbps:.1f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of 8 TB/s)")
         del g
+        if args.vendor:
+            vus = time_vendor(c)
+            row["vendor_us_per_call"] = round(vus, 3)
+            row["speedup_vs_vendor"] = round(vus / us, 3)
+            log(f"cell {row['cell']}: F.linear {vus:.3f} us/call ({vus / us:.2f}x the skinny GEMM's time)")
 
     # The dominant kernel: the compiled kernel instance that takes the largest share
     # of the step. Cells that launch the same instance are pooled, so the average

@@ -1,4 +1,4 @@
-"""BF16 skinny GEMM for MI355X (gfx950): y[M,N] = x[M,K] . W[N,K]^T for M = 1..4.
+"""BF16 skinny GEMM for MI355X (gfx950): y[M,N] = x[M,K] . W[N,K]^T for M = 1..8.
 
 Thin Python binding over the C ABI of ``libskinny_gemm_bf16.so``
 (``include/skinny_gemm.h``). Every step of the computation runs in the HIP
@@ -230,7 +230,7 @@ def _check_tensor(t: torch.Tensor, name: str, ndim: int = 2) -> None:
 
 def gemm(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
          plan: Plan | None = None, out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
-    """y = x @ W.T for bfloat16 x [M, K] (M <= 4) and W [N, K]; one kernel launch
+    """y = x @ W.T for bfloat16 x [M, K] (M <= 8) and W [N, K]; one kernel launch
     on the current stream. out_dtype torch.float32 keeps the float32 sums
     (skinny_gemm_bf16_f32out)."""
     _check_tensor(x, "x")

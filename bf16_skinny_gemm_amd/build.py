@@ -3,10 +3,13 @@
     python -m bf16_skinny_gemm_amd.build
 
 The library is built next to this file so that it travels with the source
-tree; it is never installed into site-packages.
+tree; it is never installed into site-packages. Its translation units (the host
+side and the variant tables, which hold the kernel instances) are compiled in
+parallel into objects under _build/ and linked once.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -16,9 +19,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libskinny_gemm_bf16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
+SOURCES = ("skinny_gemm.hip", "variants_fixed_small.hip", "variants_fixed_k4096.hip",
+           "variants_fixed_k8192.hip", "variants_other.hip")
+
+# hipcc's host pass warns that it does not know the packed-fp32 feature; drop that noise
+_NOISE = ("packed-fp32-ops", "not a recognized feature for this target")
 
 
 def hipcc() -> str:
@@ -28,28 +37,47 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def compile_command(out: str) -> list[str]:
+def compile_command(src: str, obj: str) -> list[str]:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-c",
         # packed-FP32 instructions are left to no one: the compiler must not form them
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-I", INCLUDE, "-I", CSRC,
-        "-o", out, os.path.join(CSRC, "skinny_gemm.hip"),
+        "-o", obj, os.path.join(CSRC, src),
     ]
 
 
-def build_library(verbose: bool = False) -> str:
-    """Compile the HIP library (always recompiles) and return its path."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = compile_command(tmp)
+def link_command(objs: list[str], out: str) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _run(cmd: list[str]) -> str:
     res = subprocess.run(cmd, cwd=HERE, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature; drop that noise
-    noise = ("packed-fp32-ops", "not a recognized feature for this target")
-    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in noise))
+    err = "\n".join(l for l in res.stderr.splitlines() if not any(n in l for n in _NOISE))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    return err
+
+
+def build_library(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile the HIP library (always recompiles) and return its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tag = f".{os.getpid()}"
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + tag + ".o") for s in SOURCES]
+    workers = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1))
+    try:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            errs = list(pool.map(_run, [compile_command(s, o) for s, o in zip(SOURCES, objs)]))
+        tmp = LIB_PATH + f".tmp{os.getpid()}"
+        errs.append(_run(link_command(objs, tmp)))
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+    if verbose:
+        for e in errs:
+            if e.strip():
+                print(e, file=sys.stderr)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -827,8 +827,8 @@ __global__ __launch_bounds__(256) void scalar_kernel(Args a)
 
 // K == 0: the empty sum, +0 for every (m, n) of y0 (and y1), rows at stride ldy;
 // elements of `elem_bytes` (2 or 4) bytes.
-__global__ __launch_bounds__(256) void zero_kernel(void *y0, void *y1, int N, int ldy, long long count,
-                                                   int elem_bytes)
+[[maybe_unused]] static __global__ __launch_bounds__(256) void zero_kernel(
+    void *y0, void *y1, int N, int ldy, long long count, int elem_bytes)
 {
     const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i < count) {

@@ -55,9 +55,14 @@ def summarise(trace_paths, filt=None):
             continue
         groups.setdefault((name, grid, wg), []).append(us)
         by_name.setdefault(name, []).append(us)
-    lines = ["dispatches  avg_us   min_us   max_us  grid(threads) wg  kernel"]
+    # p10 / median / p90 over the dispatches: the spread across weight copies (each
+    # dispatch of a cell reads a different copy)
+    lines = ["dispatches  avg_us   min_us   p10_us   med_us   p90_us   max_us  grid(threads) wg  kernel"]
     for (name, grid, wg), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"{len(v):10d} {statistics.mean(v):8.3f} {min(v):8.3f} {max(v):8.3f} "
+        q = sorted(v)
+        pick = lambda f: q[min(len(q) - 1, int(f * len(q)))]
+        lines.append(f"{len(v):10d} {statistics.mean(v):8.3f} {q[0]:8.3f} {pick(0.1):8.3f} "
+                     f"{statistics.median(q):8.3f} {pick(0.9):8.3f} {q[-1]:8.3f} "
                      f"{grid:13d} {wg:4d}  {name}")
     lines.append("")
     lines.append("per kernel name (as --stats aggregates):")

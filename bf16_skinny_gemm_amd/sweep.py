@@ -36,9 +36,9 @@ ROTATE_BYTES = 1 << 30
 # shares the bf16 plan). Paired f_b/g_b weights (4096, 128) and the TP4 pair
 # (2048, 128) are swept as pairs.
 SHAPES = [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536), (4096, 8192),
-          (77440, 4096), (6416, 4096), (19360, 4096), (38720, 4096), (288, 4096)]
+          (77440, 4096), (6416, 4096), (19360, 4096), (38720, 4096), (288, 4096), (256, 4096)]
 PAIR_SHAPES = [(4096, 128), (2048, 128)]
-MS = (1, 2, 3, 4)
+MS = (1, 2, 3, 4, 5, 6, 7, 8)
 BIG_GRID = 1 << 30  # grid_blocks >= tile count: one block per tile
 PLAN_FIELDS = ("kind", "threads_per_block", "lanes_per_row", "chunks", "rows_per_wave", "k_split",
                "nontemporal", "grid_blocks", "x_in_lds", "prefetch")
@@ -171,11 +171,21 @@ def measure(args):
     ms = tuple(int(m) for m in args.ms.split(","))
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
+    t_start = time.monotonic()
+
+    def out_of_time():
+        if args.budget and time.monotonic() - t_start > args.budget:
+            log(f"time budget of {args.budget:.0f} s spent: stopping; rerun to resume")
+            return True
+        return False
+
     with open(args.out, "a") as fout:
         for (N, K, pair) in cells:
             todo = [M for M in ms if (N, K, M, pair) not in done]
             if not todo:
                 continue
+            if out_of_time():
+                break
             wbytes = (4 if pair else 2) * N * K
             copies = max(2, math.ceil(ROTATE_BYTES / wbytes))
             base = (torch.randn((N, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
@@ -186,6 +196,8 @@ def measure(args):
                 weights = [base] + [base.clone() for _ in range(copies - 1)]
             log(f"shape ({N},{K}) pair={pair}: {copies} copies")
             for M in todo:
+                if out_of_time():
+                    break
                 x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
                 ys = ((torch.empty((M, N), dtype=torch.bfloat16, device=dev),
                        torch.empty((M, N), dtype=torch.bfloat16, device=dev)) if pair
@@ -269,6 +281,8 @@ def main():
     ap.add_argument("--refine", metavar="JSONL",
                     help="time only the --top fastest plans per cell of this earlier sweep, at --grids")
     ap.add_argument("--top", type=int, default=16)
+    ap.add_argument("--budget", type=float, default=0.0,
+                    help="stop starting new cells after this many seconds (0: no limit)")
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--replays", type=int, default=5)
     args = ap.parse_args()

@@ -15,9 +15,11 @@ linear path otherwise. Here:
 * :func:`install` swaps the forward of ``nn.Linear`` modules for the routed one.
 
 A call qualifies when x and weight are bfloat16 CUDA tensors on a gfx950 device,
-weight is [N, K] contiguous, x is [..., K] with 1 <= prod(leading dims) <= 4
-(the decode token count M), and there is no bias. The kernel itself never falls
-back: a missing library or a refused launch raises.
+weight is [N, K] contiguous, x is [..., K] with 1 <= prod(leading dims) <= 8
+(the token count M: the cited pages route 1..4; 5..8 is routed here too, since on
+MI355X the kernels measured faster than F.linear there on the decode shapes), and
+there is no bias. The kernel itself never falls back: a missing library or a
+refused launch raises.
 """
 from __future__ import annotations
 
@@ -51,17 +53,17 @@ def qualifies(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None =
     m = 1
     for d in x.shape[:-1]:
         m *= d
-    if not (1 <= m <= 4):
+    if not (1 <= m <= 8):
         return False
     return _device_is_gfx950(x.device)
 
 
 @torch.library.custom_op("skinny::linear", mutates_args=())
 def linear(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
-    """y = x @ weight.T on the HIP skinny GEMM; x [..., K] with M = prod(...) <= 4."""
+    """y = x @ weight.T on the HIP skinny GEMM; x [..., K] with M = prod(...) <= 8."""
     if not qualifies(x, weight):
         raise ValueError("skinny::linear: inputs do not qualify (bf16 on gfx950, no bias, "
-                         f"M in 1..4): x {tuple(x.shape)} {x.dtype}, weight "
+                         f"M in 1..8): x {tuple(x.shape)} {x.dtype}, weight "
                          f"{tuple(weight.shape)} {weight.dtype}")
     lib()  # raises if the HIP library is missing
     lead = x.shape[:-1]

@@ -25,10 +25,12 @@
  *    `stream` (0 = the null stream) and returns. Calls are therefore legal
  *    inside HIP graph capture. y must not overlap x or W (or, for the pair,
  *    each other).
- *  - Sizes: 0 <= M <= 4; N >= 0; K >= 0. M == 0 or N == 0 is a no-op that
+ *  - Sizes: 0 <= M <= 8; N >= 0; K >= 0. M == 0 or N == 0 is a no-op that
  *    returns SKINNY_OK (pointers may then be NULL). K == 0 writes +0 to all of
- *    y (the empty sum). M > 4 is outside the method's decode range and is
- *    rejected with SKINNY_ERR_INVALID_ARG; the caller keeps its general GEMM.
+ *    y (the empty sum). M = 1..4 is the decode range the cited plans cover;
+ *    M = 5..8 runs the same kernel families (not the MFMA one, whose A operand
+ *    has 4 rows) with tuned plans for the decode shapes. M > 8 is rejected with
+ *    SKINNY_ERR_INVALID_ARG; the caller keeps its general GEMM.
  *  - Fast path: x and W 16-byte aligned, K % 8 == 0 (128-bit weight loads)
  *    and N * (output element bytes) < 2^31. Anything else runs a correct
  *    element-wise path; it is not an error (an explicit plan that cannot run
@@ -180,10 +182,10 @@ int skinny_gemm_bf16_f32out_ex(const void *x, const void *W, float *y,
 int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out);
 
 /* Enumerates the compiled variants (grid_blocks = 0 in each). A variant covers
- * M = 1..4 except an M whose instance would exceed its register budget; a plan
- * naming it at that M returns SKINNY_ERR_UNSUPPORTED. skinny_gemm_get_variant
- * returns SKINNY_OK or SKINNY_ERR_INVALID_ARG for an index out of range.
- * Host-only. */
+ * M = 1..8 except an M whose instance would exceed its register budget (MFMA
+ * variants cover M = 1..4 only); a plan naming it at such an M returns
+ * SKINNY_ERR_UNSUPPORTED. skinny_gemm_get_variant returns SKINNY_OK or
+ * SKINNY_ERR_INVALID_ARG for an index out of range. Host-only. */
 int skinny_gemm_num_variants(void);
 int skinny_gemm_get_variant(int index, skinny_plan_t *out);
 

@@ -102,13 +102,15 @@ def _fixed_k(p):
 
 
 def test_default_plans(skg):
-    # every decode projection shape has a vector plan at every M (tuned or default)
+    # every decode projection shape has a vector plan at every M (tuned or default);
+    # the 4x4x4 MFMA family has 4 rows of A, so never beyond M = 4
     for (N, K) in [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536),
                    (4096, 8192), (77440, 4096), (4096, 128)]:
-        for M in (1, 2, 3, 4):
+        for M in range(1, 9):
             p, _ = skg.skinny_gemm_get_plan(N, K, M)
             assert p.kind in (skg.SKINNY_KIND_FIXED_K, skg.SKINNY_KIND_LOOP_K,
                               skg.SKINNY_KIND_MFMA), (N, K, M, p)
+            assert M <= 4 or p.kind != skg.SKINNY_KIND_MFMA, (N, K, M, p)
             if p.kind == skg.SKINNY_KIND_FIXED_K:
                 assert _fixed_k(p) == K
             if p.kind == skg.SKINNY_KIND_MFMA:
@@ -145,11 +147,12 @@ def test_plan_table_entries_are_valid(skg):
             assert _fixed_k(p) == K
         if p.kind == skg.SKINNY_KIND_MFMA:
             assert K % (128 * p.k_split) == 0 and (K // (128 * p.k_split)) % p.chunks == 0
-        assert 1 <= M <= 4 and p.threads_per_block // 64 % p.k_split == 0
+        assert 1 <= M <= 8 and p.threads_per_block // 64 % p.k_split == 0
+        assert M <= 4 or p.kind != skg.SKINNY_KIND_MFMA
 
 
 def test_get_plan_rejects(skg):
-    for args in ((0, 128, 1), (128, 0, 1), (128, 128, 0), (128, 128, 5)):
+    for args in ((0, 128, 1), (128, 0, 1), (128, 128, 0), (128, 128, 9)):
         with pytest.raises(skg.SkinnyError):
             skg.skinny_gemm_get_plan(*args)
     L = skg.lib()
@@ -170,7 +173,7 @@ def _call(L, *a):
 
 
 @pytest.mark.parametrize("args", [
-    (X, W, Y, 5, 16, 16, None),          # M > 4
+    (X, W, Y, 9, 16, 16, None),          # M > 8
     (X, W, Y, -1, 16, 16, None),         # negative M
     (X, W, Y, 1, -3, 16, None),          # negative N
     (X, W, Y, 1, 16, -8, None),          # negative K
@@ -193,7 +196,7 @@ def test_pair_invalid_args(skg):
         (X, W, W1, Y, None, 1, 16, 16, None),   # null y1
         (X, W, W1, Y, Y + 16, 1, 16, 16, None),  # y0 and y1 overlap
         (X, W, W1, Y, W1 + 32, 1, 16, 16, None),  # y1 overlaps W1
-        (X, W, W1, Y, Y1, 7, 16, 16, None),     # M out of range
+        (X, W, W1, Y, Y1, 9, 16, 16, None),     # M out of range
     ]
     for b in bad:
         assert L.skinny_gemm_bf16_pair(*b) == skg.SKINNY_ERR_INVALID_ARG, b

@@ -87,13 +87,18 @@ def test_module_hook_and_routing(op):
     h3 = torch.nn.functional.linear(h2, model[2].weight, model[2].bias)
     assert torch.equal(y, h3)
     assert torch.allclose(y.float(), ref[-1].float(), rtol=0.05, atol=0.05)
-    # M = 8 is outside the decode range: routed to F.linear, or refused without fallback
+    # M = 8 still takes the skinny GEMM; M = 9 is outside its range: routed to F.linear,
+    # or refused without fallback
     x8 = torch.randn(8, 512, device="cuda").to(torch.bfloat16)
-    assert not op.qualifies(x8, model[0].weight)
+    assert op.qualifies(x8, model[0].weight)
     assert torch.equal(op.skinny_linear(x8, model[0].weight),
-                       torch.nn.functional.linear(x8, model[0].weight))
+                       torch.ops.skinny.linear(x8, model[0].weight))
+    x9 = torch.randn(9, 512, device="cuda").to(torch.bfloat16)
+    assert not op.qualifies(x9, model[0].weight)
+    assert torch.equal(op.skinny_linear(x9, model[0].weight),
+                       torch.nn.functional.linear(x9, model[0].weight))
     with pytest.raises(ValueError):
-        op.skinny_linear(x8, model[0].weight, fallback=False)
+        op.skinny_linear(x9, model[0].weight, fallback=False)
 
 
 @pytest.mark.gpu
