@@ -1,8 +1,9 @@
 // Device code of the BF16 skinny GEMM for gfx950 (CDNA4, wave64).
 //
-// y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),  M <= 4 rows of x, W [N][K] row-major.
+// y[m, n] = bf16_rne( sum_k x[m, k] * W[n, k] ),  M <= 8 rows of x, W [N][K] row-major
+// (or the float32 sum itself, for the float32-output form).
 //
-// At M <= 4 the product does M flops per weight byte, so its speed is the speed
+// At M <= 8 the product does M flops per weight byte, so its speed is the speed
 // at which W streams out of HBM; vLLM PR #65306 (SM90 skinny GEMM plans), section
 // Validation, rates such kernels by weight bytes per second against the HBM
 // peak. Everything below is arranged around keeping enough 128-bit weight loads
@@ -13,15 +14,17 @@
 //    so one load instruction touches 64/LPR rows with LPR*16 contiguous bytes
 //    each. A buffer resource whose size ends at the last valid row turns the
 //    loads of rows >= N into zeros, so the N tail needs no branches;
-//  * x (at most 4 rows) stays on chip: in registers for the compile-time-K
-//    family (each lane keeps only the K positions it multiplies), in LDS for
-//    the looped-K family;
+//  * x (at most 8 rows) stays on chip: in registers (each lane keeps only the K
+//    positions it multiplies) or in LDS for the compile-time-K family, in LDS
+//    for the looped-K and matrix-core families;
 //  * products are accumulated in float32 with v_dot2c_f32_bf16 (two bf16
-//    products added into a float32 accumulator per instruction);
+//    products added into a float32 accumulator per instruction), or on the
+//    matrix cores with v_mfma_f32_4x4x4_16b_bf16 (M <= 4);
 //  * partial sums of a row meet across its LPR lanes by DPP lane permutations
 //    and row broadcasts, then across the k_split waves of a block in LDS,
 //    always in one fixed order (deterministic results);
-//  * the float32 sum is rounded once to bfloat16, nearest-even.
+//  * the float32 sum is rounded once to bfloat16, nearest-even, and stored
+//    through a buffer resource over the output row (rows >= N fall outside it).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -248,7 +251,7 @@ __device__ __forceinline__ void store_row(const Args &a, __amdgpu_buffer_rsrc_t 
 //
 // x lives in registers (XL = false: each lane keeps the M*CH 16-byte pieces it
 // multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
-// chunk reads its piece back, which frees VGPRs at M = 3, 4).
+// chunk reads its piece back, which frees VGPRs at M >= 3).
 //
 // Each block loops over the tiles of one weight (block_sched). PF selects how
 // the loop overlaps loads with arithmetic:
@@ -610,6 +613,7 @@ __device__ __forceinline__ f32x4_t mfma4x4x4(unsigned a0, unsigned a1, unsigned 
 template <int M, int U, int R, int KW, bool NT, bool PF>
 __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 {
+    static_assert(M >= 1 && M <= 4, "the 4x4x4 MFMA's A operand holds 4 rows of x");
     extern __shared__ u32x4 mx_lds[];  // x as [M][K] bfloat16
     constexpr int ROWS_W = 4 * R;
     __shared__ float part[KW > 1 ? kMaxWaves * ROWS_W * M : 1];
