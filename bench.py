@@ -19,6 +19,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -79,13 +80,22 @@ KERNEL_SOURCES = tuple(f"bf16_skinny_gemm_amd/csrc/{f}" for f in (
     "plans_gfx950.inc"))
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed (string literals
+    in these files hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
-    """Digest of the kernel sources and plan table: PMC records taken on other
-    sources no longer describe the kernels that run."""
+    """Digest of the kernel sources, variant tables and plan table, comments and
+    whitespace aside: PMC records taken on other code no longer describe the
+    kernels that run."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
