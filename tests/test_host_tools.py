@@ -1,0 +1,117 @@
+"""Host-side logic of the plan sweep and the benchmark (no GPU needed)."""
+from __future__ import annotations
+
+import json
+import os
+import re
+
+import pytest
+
+import bench
+from bf16_skinny_gemm_amd import sweep
+
+
+def _rec(N, K, M, us, **plan):
+    p = {"kind": 1, "threads_per_block": 256, "lanes_per_row": 64, "chunks": 4,
+         "rows_per_wave": 1, "k_split": 2, "nontemporal": 1, "grid_blocks": 0, "x_in_lds": 0,
+         "prefetch": 0}
+    p.update(plan)
+    return {"N": N, "K": K, "M": M, "pair": False, "plan": p, "us": us, "us_min": us,
+            "us_max": us, "gbps": 1.0}
+
+
+def test_parse_grids():
+    assert sweep.parse_grids("persistent,tile,256, 512") == (0, sweep.BIG_GRID, 256, 512)
+
+
+def test_pick_prefers_persistent_within_tolerance():
+    tile = _rec(1, 8, 1, 10.00, grid_blocks=sweep.BIG_GRID)
+    pers = _rec(1, 8, 1, 10.04, grid_blocks=0)
+    assert sweep.pick([tile, pers])["plan"]["grid_blocks"] == 0      # within 0.5%
+    slow = _rec(1, 8, 1, 10.20, grid_blocks=0)
+    assert sweep.pick([tile, slow])["plan"]["grid_blocks"] == sweep.BIG_GRID
+
+
+def test_emit_inc_one_row_per_cell(tmp_path):
+    recs = [_rec(4096, 4096, 1, 7.0, chunks=8, k_split=1), _rec(4096, 4096, 1, 6.9),
+            _rec(4096, 4096, 2, 7.5, prefetch=2, grid_blocks=512), {"N": 4096, "K": 4096,
+                                                                     "M": 2, "complete": True}]
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    out = tmp_path / "plans.inc"
+    sweep.emit_inc(str(src), str(out))
+    rows = re.findall(r"^\{(\d+), (\d+), (\d+), \{([^}]*)\}\},", out.read_text(), re.M)
+    assert [(int(a), int(b), int(c)) for a, b, c, _ in rows] == [(4096, 4096, 1), (4096, 4096, 2)]
+    fields = [int(v) for v in rows[0][3].split(",")]
+    assert fields == [1, 256, 64, 4, 1, 2, 1, 0, 0, 0]               # the 6.9 us plan
+    fields = [int(v) for v in rows[1][3].split(",")]
+    assert fields[7] == 512 and fields[9] == 2
+
+
+def test_refine_takes_top_variants_times_grids(tmp_path):
+    import bf16_skinny_gemm_amd as skg
+
+    recs = [_rec(100, 4096, 1, 5.0, grid_blocks=0), _rec(100, 4096, 1, 5.1, grid_blocks=256),
+            _rec(100, 4096, 1, 6.0, chunks=8, k_split=1), _rec(100, 4096, 1, 7.0, prefetch=2),
+            _rec(100, 4096, 2, 1.0, prefetch=1)]                     # other cell: ignored
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    plans = sweep.refine_plans(skg, str(src), 100, 4096, 1, False, 2, (0, 512))
+    got = [(p.chunks, p.k_split, p.prefetch, p.grid_blocks) for p in plans]
+    assert got == [(4, 2, 0, 0), (4, 2, 0, 512), (8, 1, 0, 0), (8, 1, 0, 512)]
+
+
+def test_kernel_names_follow_the_templates():
+    import bf16_skinny_gemm_amd as skg
+
+    p = skg.Plan.from_dict({"kind": 1, "threads_per_block": 256, "lanes_per_row": 64, "chunks": 8,
+                            "rows_per_wave": 1, "k_split": 1, "nontemporal": 1, "grid_blocks": 0,
+                            "x_in_lds": 1, "prefetch": 2})
+    assert bench.kernel_name(p, 4) == \
+        "void skg::fixed_k_kernel<4, 64, 8, 1, 1, true, true, 2>(skg::Args)"
+    p.kind, p.chunks, p.rows_per_wave = 2, 4, 2
+    assert bench.kernel_name(p, 3) == "void skg::loop_k_kernel<3, 4, 2, true>(skg::Args, int)"
+    p.kind, p.chunks, p.rows_per_wave, p.k_split, p.prefetch = 4, 2, 1, 4, 1
+    assert bench.kernel_name(p, 1) == "void skg::mfma_kernel<1, 2, 1, 4, true, true>(skg::Args)"
+    p.kind = 3
+    assert bench.kernel_name(p, 2) == "void skg::scalar_kernel<2>(skg::Args)"
+
+
+def test_kernel_names_exist_in_the_sources():
+    """The spelled templates match the kernels' parameter lists."""
+    src = open(os.path.join(bench.ROOT, "bf16_skinny_gemm_amd", "csrc", "kernels.hpp")).read()
+    for sig in (r"template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>\s*"
+                r"__global__[^\n]*fixed_k_kernel\(Args a\)",
+                r"template <int M, int U, int R, bool NT>\s*__global__[^\n]*loop_k_kernel\(Args a, int kpad\)",
+                r"template <int M, int U, int R, int KW, bool NT, bool PF>\s*__global__[^\n]*mfma_kernel\(Args a\)",
+                r"template <int M>\s*__global__[^\n]*scalar_kernel\(Args a\)"):
+        assert re.search(sig, src), sig
+
+
+def test_bytes_per_call():
+    assert bench.bytes_per_call((4096, 1024, 2)) == 2 * 4096 * 1024 + 2 * 2 * 1024 + 2 * 2 * 4096
+    assert bench.bytes_per_call(("pair", 4096, 128, 4)) == 4 * 4096 * 128 + 2 * 4 * 128 + 4 * 4 * 4096
+
+
+def test_code_only_digest_ignores_notes():
+    a = "int f() { return 1; } // one\n/* block\n comment */ int g;"
+    b = "int f()  {\n  return 1;\n}\nint g;   // changed note"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(a.replace("return 1", "return 2"))
+
+
+def test_recorded_traffic(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    kern = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, false, true, 0>(skg::Args)"
+    (prof / "traffic_kda.txt").write_text(
+        "# a note: with a colon\nsource_digest: abc\nkernel: " + kern + "\n"
+        "fetch_kib_per_dispatch: 1000\nwrite_kib_per_dispatch: 10\n"
+        "copy_fetch_factor: 2.0\ncopy_write_factor: 1.0\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda: "abc")
+    assert bench.recorded_traffic("kda", kern) == pytest.approx(1000 * 1024 * 2 + 10 * 1024)
+    assert bench.recorded_traffic("kda", kern.replace("<1,", "<2,")) is None   # other kernel
+    assert bench.recorded_traffic("mla", kern) is None                        # no record
+    monkeypatch.setattr(bench, "source_digest", lambda: "def")
+    assert bench.recorded_traffic("kda", kern) is None                        # other sources
