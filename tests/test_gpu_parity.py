@@ -316,6 +316,59 @@ def test_graph_replay_bitwise(skg):
         del g
 
 
+def test_concurrent_host_threads(skg):
+    """Entry points called from several host threads at once, each on its own stream,
+    through plans and M values whose lazily filled host caches (occupancy, static LDS,
+    raised LDS limits) are first touched concurrently: every result meets the bar."""
+    import threading
+
+    cases = []
+    for i, (N, K, M) in enumerate([(1000, 4096, 1), (777, 4096, 8), (513, 1024, 3),
+                                   (2048, 8192, 6), (300, 1536, 2), (129, 128, 7),
+                                   (4096, 4096, 5), (96, 1000, 4)]):
+        x = synth.activations(M, K, seed=140, shape_id=i)
+        W = synth.weights(N, K, seed=140, shape_id=i)
+        cases.append((x, W, to_dev(x), to_dev(W)))
+    plans = [p for p in skg.variants() if p.kind in (1, 2)]
+    results, errors = {}, []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for r in range(6):
+                    x, W, xd, Wd = cases[(t + r) % len(cases)]
+                    K = x.shape[1]
+                    # alternate the table plan with explicit grids of compiled variants
+                    cand = [p for p in plans if plan_runs_k(p, K)]
+                    plan = None
+                    if r % 2 and cand:
+                        plan = skg.Plan.from_dict({**cand[(7 * t + r) % len(cand)].as_dict(),
+                                                   "grid_blocks": 1 + (t + r) % 5})
+                    try:
+                        y = skg.gemm(xd, Wd, plan=plan)
+                    except skg.SkinnyError as e:  # this M beyond the variant's budget
+                        assert e.status == skg.SKINNY_ERR_UNSUPPORTED, str(e)
+                        y = skg.gemm(xd, Wd)
+                    s.synchronize()
+                    results[(t, r)] = (to_host(y), (t + r) % len(cases))
+        except Exception as e:  # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    assert len(results) == 48
+    for (t, r), (yb, ci) in results.items():
+        x, W, _, _ = cases[ci]
+        yr, ref, mag = oracle.gemm(x, W)
+        res = oracle.acceptance(yb, yr, ref, mag)
+        assert res["pass"], f"thread {t} call {r}: {res}"
+
+
 def test_deterministic(skg):
     N, K, M = 8192, 1536, 4
     x = to_dev(synth.activations(M, K, seed=40))
