@@ -441,10 +441,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
         }
     };
 
+    // The block's last tile is consumed outside the prefetch loops, so that no
+    // loads are issued for a tile past the end.
     auto nothing = [](int) {};
     if constexpr (PF == 2) {
         while (true) {
             const int next = sc.tile(it + step);
+            if (next >= a.tiles)
+                break;
             const __amdgpu_buffer_rsrc_t wn = F::tile_rsrc(a, wm, next, rows_t, grp);
             consume(tile, wa, [&](int j) {
 #pragma unroll
@@ -456,25 +460,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
             });
             it += step;
             tile = next;
-            if (tile >= a.tiles)
-                break;
         }
+        consume(tile, wa, nothing);
     } else if constexpr (PF == 1) {
         while (true) {
             int next = sc.tile(it + step);
+            if (next >= a.tiles) {
+                consume(tile, wa, nothing);
+                break;
+            }
             F::issue(a, wm, next, rows_t, grp, sub, kbase, wb);
             consume(tile, wa, nothing);
             it += step;
             tile = next;
-            if (tile >= a.tiles)
-                break;
             next = sc.tile(it + step);
+            if (next >= a.tiles) {
+                consume(tile, wb, nothing);
+                break;
+            }
             F::issue(a, wm, next, rows_t, grp, sub, kbase, wa);
             consume(tile, wb, nothing);
             it += step;
             tile = next;
-            if (tile >= a.tiles)
-                break;
         }
     } else {
         while (true) {
