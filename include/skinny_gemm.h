@@ -44,7 +44,9 @@
  *    share those give identical bits, and the pair gives the same bits as two
  *    single calls with the same plan.
  *  - Thread safety: every entry point may be called from any host thread; the
- *    only shared state is a per-device property cache filled once.
+ *    only shared state is host-side caches filled on first use under a lock or
+ *    with atomics (device properties; per kernel, its occupancy, static LDS
+ *    size and raised LDS limit).
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H

@@ -284,15 +284,24 @@ def test_rounding_mode_ties(skg, K):
 # ---------------------------------------------------------------------------
 
 def test_graph_replay_bitwise(skg):
-    cases = [(4096, 1024, 1), (12576, 4096, 4), (4096, 128, 2)]
+    """Every entry point captured in one graph (single, pair, strided pair over a
+    merged activation, float32 output) replays bit for bit like the eager calls, with
+    eager work between replays."""
+    cases = [(4096, 1024, 1), (12576, 4096, 4), (4096, 128, 2), (4096, 4096, 8)]
     for (N, K, M) in cases:
-        x = to_dev(synth.activations(M, K, seed=30))
+        xm = to_dev(synth.activations(M, 2 * K, seed=30))   # merged [M, 2K]
+        x = xm[:, :K].contiguous()
         W = to_dev(synth.weights(N, K, seed=30))
         W1 = to_dev(synth.weights(N, K, seed=31))
         eager = skg.gemm(x, W)
         e0, e1 = skg.gemm_pair(x, W, W1)
+        es0, es1 = skg.gemm_pair_strided(xm[:, :K], xm[:, K:], W, W1)
+        e32 = skg.gemm(x, W, out_dtype=torch.float32)
         out = torch.empty_like(eager)
         o0, o1 = torch.empty_like(e0), torch.empty_like(e1)
+        merged = torch.empty((M, 2 * N), dtype=torch.bfloat16, device="cuda")
+        s0, s1 = merged[:, :N], merged[:, N:]
+        o32 = torch.empty_like(e32)
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -301,17 +310,21 @@ def test_graph_replay_bitwise(skg):
             with torch.cuda.graph(g, stream=s):
                 skg.gemm(x, W, out=out)
                 skg.gemm_pair(x, W, W1, out0=o0, out1=o1)
+                skg.gemm_pair_strided(xm[:, :K], xm[:, K:], W, W1, out0=s0, out1=s1)
+                skg.gemm(x, W, out=o32, out_dtype=torch.float32)
         torch.cuda.current_stream().wait_stream(s)
         for rep in range(4):
-            out.zero_()
-            o0.zero_()
-            o1.zero_()
+            for t in (out, o0, o1, merged, o32):
+                t.zero_()
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), (N, K, M, rep)
             assert torch.equal(o0.view(torch.int16), e0.view(torch.int16))
             assert torch.equal(o1.view(torch.int16), e1.view(torch.int16))
+            assert torch.equal(s0.contiguous().view(torch.int16), es0.contiguous().view(torch.int16))
+            assert torch.equal(s1.contiguous().view(torch.int16), es1.contiguous().view(torch.int16))
+            assert torch.equal(o32.view(torch.int32), e32.view(torch.int32))
             _ = skg.gemm(x, W)  # eager work between replays
         del g
 
