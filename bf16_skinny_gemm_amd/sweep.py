@@ -134,7 +134,8 @@ def done_keys(path):
 
 def refine_plans(skg, path, N, K, M, pair, top, grids):
     """The `top` fastest (variant, block size) pairs of a cell in an earlier sweep
-    file, each crossed with `grids`."""
+    file, each crossed with `grids`; with grids None, the `top` fastest plans as they
+    are (grid included), to re-time the close contenders with more replays."""
     recs = []
     with open(path) as f:
         for line in f:
@@ -142,6 +143,8 @@ def refine_plans(skg, path, N, K, M, pair, top, grids):
             if "plan" in r and (r["N"], r["K"], r["M"], r["pair"]) == (N, K, M, pair):
                 recs.append(r)
     recs.sort(key=lambda r: r["us"])
+    if grids is None:
+        return [skg.Plan.from_dict(r["plan"]) for r in recs[:top]]
     seen, out = set(), []
     for r in recs:
         d = {k: v for k, v in r["plan"].items() if k != "grid_blocks"}
@@ -205,7 +208,7 @@ def measure(args):
                 nbytes = (4 * N * K + 2 * M * K + 4 * M * N) if pair else (2 * N * K + 2 * M * K + 2 * M * N)
                 best = None
                 kinds = {int(k) for k in args.kinds.split(",")} if args.kinds else None
-                grids = parse_grids(args.grids)
+                grids = None if args.grids == "same" else parse_grids(args.grids)
                 plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids) if args.refine
                          else candidate_plans(skg, K, M, kinds, grids))
                 for plan in plans:
@@ -277,7 +280,8 @@ def main():
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
     ap.add_argument("--kinds", help="comma list of plan kinds to time (default: all)")
     ap.add_argument("--grids", default="persistent,tile",
-                    help="comma list of grid modes: persistent, tile, or a block count")
+                    help="comma list of grid modes: persistent, tile, or a block count; "
+                         "with --refine, 'same' keeps each plan's own grid")
     ap.add_argument("--refine", metavar="JSONL",
                     help="time only the --top fastest plans per cell of this earlier sweep, at --grids")
     ap.add_argument("--top", type=int, default=16)

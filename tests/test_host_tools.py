@@ -115,3 +115,14 @@ def test_recorded_traffic(tmp_path, monkeypatch):
     assert bench.recorded_traffic("mla", kern) is None                        # no record
     monkeypatch.setattr(bench, "source_digest", lambda: "def")
     assert bench.recorded_traffic("kda", kern) is None                        # other sources
+
+
+def test_refine_same_grids_keeps_the_top_plans(tmp_path):
+    import bf16_skinny_gemm_amd as skg
+
+    recs = [_rec(1, 8, 1, 5.0, grid_blocks=0), _rec(1, 8, 1, 4.9, grid_blocks=512),
+            _rec(1, 8, 1, 6.0, grid_blocks=256)]
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    plans = sweep.refine_plans(skg, str(src), 1, 8, 1, False, 2, None)
+    assert [p.grid_blocks for p in plans] == [512, 0]
