@@ -211,8 +211,39 @@ def variants() -> list[Plan]:
 
 # ---- tensor helpers ---------------------------------------------------------
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(device: torch.device) -> int:
-    return int(torch.cuda.current_stream(device).cuda_stream)
+    """The raw handle of torch's current stream on `device` (no Stream object built
+    when torch exposes the raw getter)."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if _raw_stream is not None:
+        return int(_raw_stream(idx))
+    return int(torch.cuda.current_stream(idx).cuda_stream)
+
+
+class _on_device:
+    """Make `device` current for the call, switching only when it is not already."""
+
+    __slots__ = ("idx", "prev")
+
+    def __init__(self, device: torch.device):
+        self.idx = device.index
+        self.prev = None
+
+    def __enter__(self):
+        if self.idx is not None:
+            cur = torch.cuda.current_device()
+            if cur != self.idx:
+                self.prev = cur
+                torch.cuda.set_device(self.idx)
+        return self
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+        return False
 
 
 def _check_tensor(t: torch.Tensor, name: str, ndim: int = 2) -> None:
@@ -251,7 +282,7 @@ def gemm(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None = None,
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be [{M}, {N}]")
     s = _stream_handle(x.device)
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         if out_dtype == torch.float32:
             if plan is None:
                 skinny_gemm_bf16_f32out(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, s)
@@ -286,7 +317,7 @@ def gemm_pair(x: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
                 raise ValueError(f"{name} must be [{M}, {N}]")
         outs.append(o)
     s = _stream_handle(x.device)
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         if plan is None:
             skinny_gemm_bf16_pair(x.data_ptr(), W0.data_ptr(), W1.data_ptr(), outs[0].data_ptr(),
                                   outs[1].data_ptr(), M, N, K, s)
@@ -334,7 +365,7 @@ def gemm_pair_strided(x0: torch.Tensor, x1: torch.Tensor, W0: torch.Tensor, W1: 
     ldx = x0.stride(0) if M > 1 else K
     ldy = out0.stride(0) if M > 1 else N
     s = _stream_handle(x0.device)
-    with torch.cuda.device(x0.device):
+    with _on_device(x0.device):
         args = (x0.data_ptr(), x1.data_ptr(), ldx, W0.data_ptr(), W1.data_ptr(), out0.data_ptr(),
                 out1.data_ptr(), ldy, M, N, K)
         if plan is None:

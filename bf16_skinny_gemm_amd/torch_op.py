@@ -27,7 +27,7 @@ import functools
 
 import torch
 
-from . import gemm, lib
+from . import _on_device, _stream_handle, skinny_gemm_bf16
 
 _ARCH_OK: dict[int, bool] = {}
 
@@ -65,13 +65,19 @@ def linear(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
         raise ValueError("skinny::linear: inputs do not qualify (bf16 on gfx950, no bias, "
                          f"M in 1..8): x {tuple(x.shape)} {x.dtype}, weight "
                          f"{tuple(weight.shape)} {weight.dtype}")
-    lib()  # raises if the HIP library is missing
-    lead = x.shape[:-1]
     K = x.shape[-1]
-    x2 = x.reshape(-1, K).contiguous()
-    w = weight.contiguous()
-    y = gemm(x2, w)
-    return y.reshape(*lead, w.shape[0])
+    N = weight.shape[0]
+    x2 = x.reshape(-1, K)
+    if not x2.is_contiguous():
+        x2 = x2.contiguous()
+    w = weight if weight.is_contiguous() else weight.contiguous()
+    y = torch.empty((*x.shape[:-1], N), dtype=torch.bfloat16, device=x.device)
+    # qualifies() has checked dtypes, devices and shapes: call the C entry point
+    # directly (it raises if the library is missing or refuses the call)
+    with _on_device(x.device):
+        skinny_gemm_bf16(x2.data_ptr(), w.data_ptr(), y.data_ptr(), x2.shape[0], N, K,
+                         _stream_handle(x.device))
+    return y
 
 
 @linear.register_fake
