@@ -234,7 +234,7 @@ def _exact(skg, x, W, label):
 @pytest.mark.parametrize("K", [128, 1024, 1536, 4096, 8192, 1000, 37])
 def test_exact_special_cases(skg, K):
     g = np.random.default_rng(K)
-    for M in (1, 4):
+    for M in (1, 4, 8):
         x = synth.activations(M, K, seed=20, shape_id=K)
         # zero weight
         _exact(skg, x, np.zeros((70, K), np.uint16), f"zero K={K}")
@@ -277,6 +277,13 @@ def test_rounding_mode_ties(skg, K):
     W[:, :2] = bits([-1.0, -1.0])
     y = to_host(skg.gemm(to_dev(x), to_dev(W)))
     assert np.all(y[0] == 0xBF80) and np.all(y[1] == 0xBF82)
+    # M = 8: the two ties alternate over all eight rows of the output
+    x8 = np.zeros((8, K), np.uint16)
+    x8[0::2] = x[0]
+    x8[1::2] = x[1]
+    W[:, :2] = synth.BF16_ONE
+    y = to_host(skg.gemm(to_dev(x8), to_dev(W)))
+    assert np.all(y[0::2] == 0x3F80) and np.all(y[1::2] == 0x3F82), [hex(v) for v in y.ravel()]
 
 
 # ---------------------------------------------------------------------------
@@ -428,17 +435,31 @@ def test_same_reduction_order_same_bits(skg):
 
 
 def test_guard_band(skg):
-    """Outputs are written only inside y: sentinels around it stay untouched."""
-    for (N, K, M) in [(4096 + 3, 1024, 3), (300, 128, 4), (77, 1000, 2), (65, 13, 1)]:
-        pad = 4096
-        buf = torch.full((M * N + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
-        y = buf[pad:pad + M * N].view(M, N)
-        x = synth.activations(M, K, seed=50, shape_id=N)
-        W = synth.weights(N, K, seed=50, shape_id=N)
-        skg.gemm(to_dev(x), to_dev(W), out=y)
-        torch.cuda.synchronize()
-        assert torch.all(buf[:pad] == -7.0) and torch.all(buf[pad + M * N:] == -7.0)
-        check(y, x, W, label=f"guard N={N} K={K}")
+    """Outputs are written only inside y: sentinels around it stay untouched, for the
+    table's plans, one explicit plan of each vector family at a ragged N, and the
+    float32 output."""
+    fams = {}
+    for p in skg.variants():
+        if p.kind in (1, 2, 4) and p.kind not in fams and plan_runs_k(p, 4096):
+            fams[p.kind] = p
+    cases = [(4096 + 3, 1024, 3, None), (300, 128, 4, None), (77, 1000, 2, None),
+             (65, 13, 1, None), (129, 4096, 8, None)]
+    cases += [(4 * rows_per_tile(p) + 5, 4096, 3, p) for p in fams.values()]
+    for (N, K, M, plan) in cases:
+        for dt in (torch.bfloat16, torch.float32):
+            pad = 4096
+            buf = torch.full((M * N + 2 * pad,), -7.0, dtype=dt, device="cuda")
+            y = buf[pad:pad + M * N].view(M, N)
+            x = synth.activations(M, K, seed=50, shape_id=N)
+            W = synth.weights(N, K, seed=50, shape_id=N)
+            skg.gemm(to_dev(x), to_dev(W), out=y, plan=plan, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert torch.all(buf[:pad] == -7.0) and torch.all(buf[pad + M * N:] == -7.0), \
+                (N, K, M, plan, dt)
+            if dt == torch.bfloat16:
+                check(y, x, W, label=f"guard N={N} K={K} M={M} {plan}")
+            else:
+                check_f32(y, x, W, label=f"guard f32 N={N} K={K} M={M} {plan}")
 
 
 # ---------------------------------------------------------------------------
@@ -510,7 +531,7 @@ def test_robustness_inputs(skg, kind):
     """Input classes beyond normal (vLLM PR #65306, section Validation): outlier,
     scaled and sparse."""
     for (N, K) in [(4096, 1024), (2048, 4096), (8192, 1536)]:
-        for M in (1, 4):
+        for M in (1, 4, 8):
             if kind == "outlier":
                 x = synth.outlier_activations(M, K, seed=70, shape_id=N)
             elif kind == "scaled_up":
