@@ -156,7 +156,7 @@ def kernel_name(p, M) -> str:
     """The kernel instance a plan launches, spelled as rocprofv3 prints it."""
     nt = "true" if p.nontemporal else "false"
     if p.kind == 1:
-        xl = "true" if p.x_in_lds else "false"
+        xl = p.x_in_lds
         return (f"void skg::fixed_k_kernel<{M}, {p.lanes_per_row}, {p.chunks}, {p.rows_per_wave}, "
                 f"{p.k_split}, {xl}, {nt}, {p.prefetch}>(skg::Args)")
     if p.kind == 2:

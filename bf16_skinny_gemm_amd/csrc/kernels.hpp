@@ -249,9 +249,10 @@ __device__ __forceinline__ void store_row(const Args &a, __amdgpu_buffer_rsrc_t 
 // (lane / LPR, lane % LPR) reads, for row r*RPI + sub of its group and chunk
 // j < CH, the 8 elements starting at  kw * K/KW + j * LPR*8 + kl * 8.
 //
-// x lives in registers (XL = false: each lane keeps the M*CH 16-byte pieces it
-// multiplies) or in LDS (XL = true: the block stages x[M][K] once and every
-// chunk reads its piece back, which frees VGPRs at M >= 3).
+// x lives in registers (XL = 0: each lane keeps the M*CH 16-byte pieces it
+// multiplies) or in LDS (XL = 1 or 2: the block stages x[M][K] once and every
+// chunk reads its pieces back, which frees VGPRs at M >= 3; with XL = 2 the
+// pieces of a chunk are read one chunk ahead of their use).
 //
 // Each block loops over the tiles of one weight (block_sched). PF selects how
 // the loop overlaps loads with arithmetic:
@@ -268,7 +269,7 @@ __device__ __forceinline__ void store_row(const Args &a, __amdgpu_buffer_rsrc_t 
 // ---------------------------------------------------------------------------
 constexpr int kMaxWaves = 8;  // largest block: 512 threads
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
+template <int M, int LPR, int CH, int R, int KW, int XL, bool NT, int PF>
 struct FixedK {
     static constexpr int K = KW * LPR * 8 * CH;
     static constexpr int KSLICE = K / KW;
@@ -312,7 +313,7 @@ struct FixedK {
     }
 };
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
+template <int M, int LPR, int CH, int R, int KW, int XL, bool NT, int PF>
 __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 {
     using F = FixedK<M, LPR, CH, R, KW, XL, NT, PF>;
@@ -381,26 +382,48 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 acc[m][r] = 0.0f;
+        // x from LDS: XL = 1 reads chunk j's pieces at chunk j; XL = 2 reads them
+        // one chunk ahead (before chunk j-1 is multiplied), so the LDS latency
+        // hides behind those products, at the price of M more 16-byte registers.
+        // volatile: keep each LDS read in its chunk; hoisting them out of the
+        // tile loop would rebuild the register copy of x that XL avoids.
+        const volatile __attribute__((address_space(3))) u32x4 *xp =
+            (const volatile __attribute__((address_space(3))) u32x4 *)x_lds;
+        u32x4 xc[XL == 2 ? M : 1], xn[XL == 2 ? M : 1];
+        auto read_x = [&](int j, u32x4 (&dst)[XL == 2 ? M : 1]) {
 #pragma unroll
-        for (int j = 0; j < CH; ++j)
+            for (int m = 0; m < (XL == 2 ? M : 1); ++m)
+                dst[m] = xp[(m * K + (int)kbase + j * LPR * 8) / 8];
+        };
+        if constexpr (XL == 2)
+            read_x(0, xc);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if constexpr (XL == 2) {
+                if (j + 1 < CH)
+                    read_x(j + 1, xn);
+            }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 u32x4 xv;
-                if constexpr (XL) {
-                    // volatile: keep the LDS read here; hoisting it out of the tile
-                    // loop would rebuild the register copy of x that XL avoids
-                    const volatile __attribute__((address_space(3))) u32x4 *xp =
-                        (const volatile __attribute__((address_space(3))) u32x4 *)x_lds;
+                if constexpr (XL == 2)
+                    xv = xc[m];
+                else if constexpr (XL == 1)
                     xv = xp[(m * K + (int)kbase + j * LPR * 8) / 8];
-                } else {
+                else
                     xv = xr[m][j];
-                }
 #pragma unroll
                 for (int r = 0; r < R; ++r)
                     acc[m][r] = dot8(wv[r][j], xv, acc[m][r]);
                 if (m == M - 1)
                     after_chunk(j);
             }
+            if constexpr (XL == 2) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    xc[m] = xn[m];
+            }
+        }
 #pragma unroll
         for (int m = 0; m < M; ++m)
 #pragma unroll

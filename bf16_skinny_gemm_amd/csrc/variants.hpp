@@ -27,14 +27,18 @@ struct Variant {
 
 // Register budget per lane, so that no instance spills: x in registers takes
 // 4*M*CH VGPRs (at most 128), the weight sets in flight 4*R*CH each (two with
-// tile prefetch, one without or with rolling prefetch).
-constexpr bool fits(int M, int CH, int R, bool XL, int PF)
+// tile prefetch, one without or with rolling prefetch). Reading x from LDS one
+// chunk ahead (XL = 2) holds 4*M more and is built for M >= 2 only: at M = 1 a
+// register copy of x is cheaper.
+constexpr bool fits(int M, int CH, int R, int XL, int PF)
 {
     const int w = (PF == 1 ? 2 : 1) * R * CH;
+    if (XL == 2)
+        return M >= 2 && w <= 20;
     return XL ? w <= 20 : (M * CH <= 32 && M * CH + w <= 48);
 }
 
-template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
+template <int M, int LPR, int CH, int R, int KW, int XL, bool NT, int PF>
 constexpr const void *fixed_fn()
 {
     if constexpr (fits(M, CH, R, XL, PF))
@@ -43,11 +47,11 @@ constexpr const void *fixed_fn()
         return nullptr;
 }
 
-template <int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>
+template <int LPR, int CH, int R, int KW, int XL, bool NT, int PF>
 Variant fixed_variant()
 {
     Variant v{};
-    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL ? 1 : 0, PF};
+    v.plan = skinny_plan_t{SKINNY_KIND_FIXED_K, 256, LPR, CH, R, KW, NT ? 1 : 0, 0, XL, PF};
     v.fn[0] = fixed_fn<1, LPR, CH, R, KW, XL, NT, PF>();
     v.fn[1] = fixed_fn<2, LPR, CH, R, KW, XL, NT, PF>();
     v.fn[2] = fixed_fn<3, LPR, CH, R, KW, XL, NT, PF>();
@@ -113,15 +117,16 @@ inline Variant scalar_variant()
 
 // Per (lanes_per_row, chunks, k_split): one or two rows per wave, x in registers
 // or LDS, each prefetch mode (none, tile, rolling), all with the non-temporal
-// hint; plus the plain-cached form at one row per wave (the hint won every cell
-// of the gfx950 sweep).
+// hint; x in LDS read one chunk ahead at one row per wave; plus the plain-cached
+// form at one row per wave (the hint won every cell of the gfx950 sweep).
 #define SKG_FIXED_XP(LPR, CH, KW, XL, PF)                                                          \
     fixed_variant<LPR, CH, 1, KW, XL, true, PF>(), fixed_variant<LPR, CH, 2, KW, XL, true, PF>()
 #define SKG_FIXED(LPR, CH, KW)                                                                      \
-    SKG_FIXED_XP(LPR, CH, KW, false, 0), SKG_FIXED_XP(LPR, CH, KW, false, 1),                       \
-        SKG_FIXED_XP(LPR, CH, KW, false, 2), SKG_FIXED_XP(LPR, CH, KW, true, 0),                    \
-        SKG_FIXED_XP(LPR, CH, KW, true, 1), SKG_FIXED_XP(LPR, CH, KW, true, 2),                     \
-        fixed_variant<LPR, CH, 1, KW, false, false, 1>()
+    SKG_FIXED_XP(LPR, CH, KW, 0, 0), SKG_FIXED_XP(LPR, CH, KW, 0, 1),                               \
+        SKG_FIXED_XP(LPR, CH, KW, 0, 2), SKG_FIXED_XP(LPR, CH, KW, 1, 0),                           \
+        SKG_FIXED_XP(LPR, CH, KW, 1, 1), SKG_FIXED_XP(LPR, CH, KW, 1, 2),                           \
+        fixed_variant<LPR, CH, 1, KW, 2, true, 0>(), fixed_variant<LPR, CH, 1, KW, 2, true, 1>(),   \
+        fixed_variant<LPR, CH, 1, KW, 2, true, 2>(), fixed_variant<LPR, CH, 1, KW, 0, false, 1>()
 #define SKG_LOOP(U, R) loop_variant<U, R, false>(), loop_variant<U, R, true>()
 #define SKG_MFMA_PF(U, R, KW) mfma_variant<U, R, KW, false>(), mfma_variant<U, R, KW, true>()
 #define SKG_MFMA(U, R) SKG_MFMA_PF(U, R, 1), SKG_MFMA_PF(U, R, 2), SKG_MFMA_PF(U, R, 4), SKG_MFMA_PF(U, R, 8)

@@ -132,10 +132,19 @@ def done_keys(path):
     return keys
 
 
-def refine_plans(skg, path, N, K, M, pair, top, grids):
+def lookahead_twin(d, M):
+    """The same fixed-K plan with x in LDS read one chunk ahead (x_in_lds 2), for
+    plans with one row per wave at M >= 2 (the only ones compiled), else None."""
+    if d["kind"] != 1 or d["rows_per_wave"] != 1 or d["x_in_lds"] == 2 or M < 2:
+        return None
+    return {**d, "x_in_lds": 2}
+
+
+def refine_plans(skg, path, N, K, M, pair, top, grids, twins=False):
     """The `top` fastest (variant, block size) pairs of a cell in an earlier sweep
     file, each crossed with `grids`; with grids None, the `top` fastest plans as they
-    are (grid included), to re-time the close contenders with more replays."""
+    are (grid included), to re-time the close contenders with more replays. With
+    `twins`, each plan's lookahead twin (lookahead_twin) is timed after it."""
     recs = []
     with open(path) as f:
         for line in f:
@@ -144,17 +153,27 @@ def refine_plans(skg, path, N, K, M, pair, top, grids):
                 recs.append(r)
     recs.sort(key=lambda r: r["us"])
     if grids is None:
-        return [skg.Plan.from_dict(r["plan"]) for r in recs[:top]]
-    seen, out = set(), []
-    for r in recs:
-        d = {k: v for k, v in r["plan"].items() if k != "grid_blocks"}
-        key = tuple(sorted(d.items()))
-        if key in seen:
-            continue
-        seen.add(key)
-        out.extend(skg.Plan.from_dict({**d, "grid_blocks": g}) for g in grids)
-        if len(seen) >= top:
-            break
+        dicts = [r["plan"] for r in recs[:top]]
+    else:
+        seen, dicts = set(), []
+        for r in recs:
+            d = {k: v for k, v in r["plan"].items() if k != "grid_blocks"}
+            key = tuple(sorted(d.items()))
+            if key in seen:
+                continue
+            seen.add(key)
+            dicts.extend({**d, "grid_blocks": g} for g in grids)
+            if len(seen) >= top:
+                break
+    out, keys = [], set()
+    for d in dicts:
+        for cand in (d, lookahead_twin(d, M) if twins else None):
+            if cand is None:
+                continue
+            key = tuple(sorted(cand.items()))
+            if key not in keys:
+                keys.add(key)
+                out.append(skg.Plan.from_dict(cand))
     return out
 
 
@@ -209,8 +228,8 @@ def measure(args):
                 best = None
                 kinds = {int(k) for k in args.kinds.split(",")} if args.kinds else None
                 grids = None if args.grids == "same" else parse_grids(args.grids)
-                plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids) if args.refine
-                         else candidate_plans(skg, K, M, kinds, grids))
+                plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids, args.twins)
+                         if args.refine else candidate_plans(skg, K, M, kinds, grids))
                 for plan in plans:
                     try:
                         us, lo, hi = time_plan(torch, skg, x, weights, ys, plan, pair,
@@ -285,6 +304,8 @@ def main():
     ap.add_argument("--refine", metavar="JSONL",
                     help="time only the --top fastest plans per cell of this earlier sweep, at --grids")
     ap.add_argument("--top", type=int, default=16)
+    ap.add_argument("--twins", action="store_true",
+                    help="with --refine, also time each plan with x read from LDS one chunk ahead")
     ap.add_argument("--budget", type=float, default=0.0,
                     help="stop starting new cells after this many seconds (0: no limit)")
     ap.add_argument("--trials", type=int, default=3)

@@ -98,9 +98,11 @@ typedef struct skinny_plan {
                                   units x blocks resident per unit), each block looping over
                                   tiles; > 0: at most this many blocks (a value >= the tile
                                   count gives one block per tile) */
-    int32_t x_in_lds;          /* FIXED_K: 1 = x staged once per block in LDS, 0 = each lane
-                                  keeps its slice of x in registers; LOOP_K, MFMA: always 1;
-                                  SCALAR: always 0 */
+    int32_t x_in_lds;          /* FIXED_K: 1 = x staged once per block in LDS, each chunk's
+                                  pieces read back when the chunk is multiplied; 2 = the
+                                  same, read one chunk ahead (one row per wave, M >= 2);
+                                  0 = each lane keeps its slice of x in registers;
+                                  LOOP_K, MFMA: always 1; SCALAR: always 0 */
     int32_t prefetch;          /* FIXED_K, MFMA: 1 = the next tile's (MFMA: the next K batch's)
                                   weights are loaded while the current one is consumed (two
                                   register sets); 0 = one at a time. FIXED_K also 2 = rolling:

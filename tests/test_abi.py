@@ -225,11 +225,20 @@ def test_ex_rejects_bad_plans(skg):
              k_split=1, nontemporal=1, grid_blocks=0, prefetch=1)
     assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 2048, ctypes.byref(p), None) == \
         skg.SKINNY_ERR_INVALID_ARG
-    # x_in_lds must be 0 or 1
+    # x_in_lds: 0, 1 or 2 for a fixed-K plan, 1 for looped-K
+    p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
+             k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=3, prefetch=1)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 2, 16, 1024, ctypes.byref(p), None) in \
+        (skg.SKINNY_ERR_INVALID_ARG, skg.SKINNY_ERR_UNSUPPORTED)
+    p = Plan(kind=2, threads_per_block=256, lanes_per_row=64, chunks=4, rows_per_wave=1,
+             k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=2)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 2, 16, 1024, ctypes.byref(p), None) in \
+        (skg.SKINNY_ERR_INVALID_ARG, skg.SKINNY_ERR_UNSUPPORTED)
+    # x read one chunk ahead is compiled for M >= 2 only
     p = Plan(kind=1, threads_per_block=256, lanes_per_row=64, chunks=2, rows_per_wave=1,
              k_split=1, nontemporal=1, grid_blocks=0, x_in_lds=2, prefetch=1)
-    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) in \
-        (skg.SKINNY_ERR_INVALID_ARG, skg.SKINNY_ERR_UNSUPPORTED)
+    assert L.skinny_gemm_bf16_ex(X, W, Y, 1, 16, 1024, ctypes.byref(p), None) == \
+        skg.SKINNY_ERR_UNSUPPORTED
     # block size not a multiple of 64 * k_split, too large, negative grid
     for tpb, ks, ch, grid in ((96, 1, 2, 0), (1024, 1, 2, 0), (64, 2, 1, 0), (256, 1, 2, -1)):
         p = Plan(kind=1, threads_per_block=tpb, lanes_per_row=64, chunks=ch, rows_per_wave=1,

@@ -68,7 +68,7 @@ def test_kernel_names_follow_the_templates():
                             "rows_per_wave": 1, "k_split": 1, "nontemporal": 1, "grid_blocks": 0,
                             "x_in_lds": 1, "prefetch": 2})
     assert bench.kernel_name(p, 4) == \
-        "void skg::fixed_k_kernel<4, 64, 8, 1, 1, true, true, 2>(skg::Args)"
+        "void skg::fixed_k_kernel<4, 64, 8, 1, 1, 1, true, 2>(skg::Args)"
     p.kind, p.chunks, p.rows_per_wave = 2, 4, 2
     assert bench.kernel_name(p, 3) == "void skg::loop_k_kernel<3, 4, 2, true>(skg::Args, int)"
     p.kind, p.chunks, p.rows_per_wave, p.k_split, p.prefetch = 4, 2, 1, 4, 1
@@ -80,7 +80,7 @@ def test_kernel_names_follow_the_templates():
 def test_kernel_names_exist_in_the_sources():
     """The spelled templates match the kernels' parameter lists."""
     src = open(os.path.join(bench.ROOT, "bf16_skinny_gemm_amd", "csrc", "kernels.hpp")).read()
-    for sig in (r"template <int M, int LPR, int CH, int R, int KW, bool XL, bool NT, int PF>\s*"
+    for sig in (r"template <int M, int LPR, int CH, int R, int KW, int XL, bool NT, int PF>\s*"
                 r"__global__[^\n]*fixed_k_kernel\(Args a\)",
                 r"template <int M, int U, int R, bool NT>\s*__global__[^\n]*loop_k_kernel\(Args a, int kpad\)",
                 r"template <int M, int U, int R, int KW, bool NT, bool PF>\s*__global__[^\n]*mfma_kernel\(Args a\)",
@@ -103,7 +103,7 @@ def test_code_only_digest_ignores_notes():
 def test_recorded_traffic(tmp_path, monkeypatch):
     prof = tmp_path / "profiles"
     prof.mkdir()
-    kern = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, false, true, 0>(skg::Args)"
+    kern = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, 0, true, 0>(skg::Args)"
     (prof / "traffic_kda.txt").write_text(
         "# a note: with a colon\nsource_digest: abc\nkernel: " + kern + "\n"
         "fetch_kib_per_dispatch: 1000\nwrite_kib_per_dispatch: 10\n"
@@ -126,3 +126,22 @@ def test_refine_same_grids_keeps_the_top_plans(tmp_path):
     src.write_text("".join(json.dumps(r) + "\n" for r in recs))
     plans = sweep.refine_plans(skg, str(src), 1, 8, 1, False, 2, None)
     assert [p.grid_blocks for p in plans] == [512, 0]
+
+
+def test_refine_twins_add_the_lookahead_form(tmp_path):
+    import bf16_skinny_gemm_amd as skg
+
+    recs = [_rec(1, 8, 2, 5.0, x_in_lds=1, grid_blocks=512),
+            _rec(1, 8, 2, 5.1, rows_per_wave=2, x_in_lds=1),             # two rows: no twin
+            _rec(1, 8, 2, 5.2, x_in_lds=0, prefetch=2),
+            _rec(1, 8, 2, 5.3, x_in_lds=2, grid_blocks=512),             # already a twin
+            _rec(1, 8, 1, 4.0, x_in_lds=1)]                              # M = 1: no twin
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    plans = sweep.refine_plans(skg, str(src), 1, 8, 2, False, 4, None, twins=True)
+    got = [(p.rows_per_wave, p.x_in_lds, p.prefetch, p.grid_blocks) for p in plans]
+    assert got == [(1, 1, 0, 512), (1, 2, 0, 512), (2, 1, 0, 0), (1, 0, 2, 0), (1, 2, 2, 0)]
+    plans = sweep.refine_plans(skg, str(src), 1, 8, 1, False, 4, None, twins=True)
+    assert [(p.x_in_lds, p.grid_blocks) for p in plans] == [(1, 0)]
+    plans = sweep.refine_plans(skg, str(src), 1, 8, 2, False, 1, (0, 256), twins=True)
+    assert [(p.x_in_lds, p.grid_blocks) for p in plans] == [(1, 0), (2, 0), (1, 256), (2, 256)]
