@@ -71,6 +71,10 @@ def parse():
                          "cell under the same graph protocol (informational)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 256 MiB (PMC counter calibration)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the read-stream ceiling: the read-only probe kernel at "
+                         "64 MiB, 256 MiB and 1 GiB per read (rotated over >= 1 GiB), both cache "
+                         "hints, several grids; a line fit gives rate and fixed cost per launch")
     return ap.parse_args()
 
 
@@ -138,12 +142,107 @@ def copy_calibration() -> int:
     return 0
 
 
+def fit_line(xs, ys):
+    """Least-squares y = a + b x; returns (a, b)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    return my - b * mx, b
+
+
+def read_ceiling(args) -> int:
+    """HBM read rate of a kernel that only reads (libskinny_stream_probe.so), the
+    practical ceiling beside which the GEMV's weight stream is judged. Reads of
+    64 MiB, 256 MiB and 1 GiB, each size rotated over >= 1 GiB of views into one
+    2 GiB buffer (past the 256 MB Infinity Cache), one graph of reads per (size,
+    cache hint, grid), timed like the cells. Time against bytes is fitted with a
+    line: the slope is the streaming rate, the intercept the fixed cost of a
+    launch (start-up, ramp and drain)."""
+    import torch
+
+    from bf16_skinny_gemm_amd import probe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pool = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    pool.fill_(1)
+    sizes = (64 << 20, 256 << 20, 1 << 30)
+    rows, fits = [], []
+    chunk = 32 << 10  # the probe's chunk: grid 0 below means one block per chunk
+    for nt in (True, False):
+        for grid_mode in (1024, 2048, 4096, 0):
+            per_size = []
+            for size in sizes:
+                grid = grid_mode or min(65536, size // chunk)
+                sink = torch.empty(probe.sink_words(grid), dtype=torch.int32, device=dev)
+                views = [pool[i * size:(i + 1) * size] for i in range(max(2, (1 << 30) // size))]
+
+                def run(views=views, sink=sink, nt=nt, grid=grid):
+                    for v in views:
+                        probe.read(v, sink, nontemporal=nt, grid_blocks=grid)
+
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(s):
+                    run()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=s):
+                        run()
+                torch.cuda.current_stream().wait_stream(s)
+                g.replay()
+                torch.cuda.synchronize()
+                per = []
+                for _ in range(args.trials):
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(args.replays):
+                        g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    per.append(e0.elapsed_time(e1) * 1e3 / (args.replays * len(views)))
+                us = statistics.median(per)
+                per_size.append(us)
+                rows.append({"nontemporal": int(nt), "grid_blocks": grid, "bytes": size,
+                             "us_per_read": round(us, 2), "gbps": round(size / (us * 1e-6) / 1e9, 1)})
+                log(f"read probe nt={int(nt)} grid={grid} {size >> 20} MiB: {us:.2f} us, "
+                    f"{rows[-1]['gbps']} GB/s")
+                del g
+            a, b = fit_line(list(sizes), per_size)
+            fits.append({"nontemporal": int(nt), "grid": grid_mode or "one block per chunk",
+                         "stream_gbps": round(1e-3 / b, 1), "fixed_us": round(a, 2)})
+            log(f"fit nt={int(nt)} grid={fits[-1]['grid']}: {fits[-1]['stream_gbps']} GB/s + "
+                f"{a:.2f} us per launch")
+    best = max(fits, key=lambda f: f["stream_gbps"])
+    print(json.dumps({"read_ceiling_gbps": best["stream_gbps"], "best_fit": best, "fits": fits,
+                      "runs": rows}), flush=True)
+    return 0
+
+
 def bytes_per_call(cell) -> int:
     if cell[0] == "pair":
         _, N, K, M = cell
         return 4 * N * K + 2 * M * K + 4 * M * N
     N, K, M = cell
     return 2 * N * K + 2 * M * K + 2 * M * N
+
+
+def weight_bytes(cell) -> int:
+    """The weight alone, the rate vLLM PR #65306 (section Validation) quotes."""
+    if cell[0] == "pair":
+        return 4 * cell[1] * cell[2]
+    return 2 * cell[0] * cell[1]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cell_name(cell) -> str:
@@ -179,6 +278,8 @@ def main() -> int:
 
     if args.copy_calibration:
         return copy_calibration()
+    if args.read_ceiling:
+        return read_ceiling(args)
 
     import numpy as np
     import torch
@@ -345,6 +446,7 @@ def main() -> int:
         row = {"cell": cell_name(c["cell"]), "us_per_call": round(us, 3),
                "us_min": round(min(per_call), 3), "us_max": round(max(per_call), 3),
                "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+               "weight_gbps": round(weight_bytes(c["cell"]) / (us * 1e-6) / 1e9, 1),
                "bytes_per_call": b, "calls_per_replay": c["calls"]}
         if c["cell"][0] == "pair":
             _, N, K, M = c["cell"]
@@ -436,7 +538,7 @@ def main() -> int:
                 done_bytes += bytes_per_call(cell)
             passes += 1
         cpu = {"value": round(done_bytes / t_cpu / 1e9, 3), "unit": "GB/s", "cores": nt,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"{passes} pass(es) of one call per cell of the workload "
                          f"({len(cells)} cells), fp64 C oracle, {t_cpu:.1f} s"}
         log(f"cpu oracle: {cpu}")

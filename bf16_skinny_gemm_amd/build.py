@@ -5,7 +5,9 @@
 The library is built next to this file so that it travels with the source
 tree; it is never installed into site-packages. Its translation units (the host
 side and the variant tables, which hold the kernel instances) are compiled in
-parallel into objects under _build/ and linked once.
+parallel into objects under _build/ and linked once. The read-stream probe used
+by the benchmark (include/skinny_stream_probe.h) is built beside it as
+libskinny_stream_probe.so.
 """
 from __future__ import annotations
 
@@ -25,6 +27,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 SOURCES = ("skinny_gemm.hip", "variants_fixed_small.hip", "variants_fixed_k4096.hip",
            "variants_fixed_k8192.hip", "variants_other.hip")
+PROBE_LIB_PATH = os.path.join(HERE, "libskinny_stream_probe.so")
+PROBE_SOURCES = ("stream_probe.hip",)
 
 # hipcc's host pass warns that it does not know the packed-fp32 feature; drop that noise
 _NOISE = ("packed-fp32-ops", "not a recognized feature for this target")
@@ -60,16 +64,19 @@ def _run(cmd: list[str]) -> str:
 
 
 def build_library(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile the HIP library (always recompiles) and return its path."""
+    """Compile the HIP library and the read-stream probe (always recompiles) and
+    return the library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     tag = f".{os.getpid()}"
-    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + tag + ".o") for s in SOURCES]
-    workers = jobs or max(1, min(len(SOURCES), os.cpu_count() or 1))
+    sources = SOURCES + PROBE_SOURCES
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + tag + ".o") for s in sources]
+    workers = jobs or max(1, min(len(sources), os.cpu_count() or 1))
+    outs = ((LIB_PATH, objs[:len(SOURCES)]), (PROBE_LIB_PATH, objs[len(SOURCES):]))
     try:
         with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
-            errs = list(pool.map(_run, [compile_command(s, o) for s, o in zip(SOURCES, objs)]))
-        tmp = LIB_PATH + f".tmp{os.getpid()}"
-        errs.append(_run(link_command(objs, tmp)))
+            errs = list(pool.map(_run, [compile_command(s, o) for s, o in zip(sources, objs)]))
+        for path, part in outs:
+            errs.append(_run(link_command(part, path + f".tmp{os.getpid()}")))
     finally:
         for o in objs:
             if os.path.exists(o):
@@ -78,7 +85,8 @@ def build_library(verbose: bool = False, jobs: int | None = None) -> str:
         for e in errs:
             if e.strip():
                 print(e, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    for path, _ in outs:
+        os.replace(path + f".tmp{os.getpid()}", path)
     return LIB_PATH
 
 

@@ -1,0 +1,94 @@
+// libskinny_stream_probe.so: one pass over a device buffer with 16-byte buffer
+// loads and nothing else, to measure the read rate HBM gives a plain streaming
+// kernel on this device (include/skinny_stream_probe.h). Measurement only.
+#include "skinny_stream_probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;                                   // 16-byte loads per thread per chunk
+constexpr unsigned kChunk = kThreads * 16u * kUnroll;        // 32 KiB
+
+// The buffer is cut into 32 KiB chunks dealt to the blocks round-robin (chunk c
+// to block c mod grid), the order in which the GEMV's persistent blocks take
+// their tiles, so the blocks sweep the buffer side by side. Each chunk is read
+// through a buffer resource over exactly its bytes (the last chunk's loads past
+// the end read zeros, the XOR identity), and the next chunk's loads are issued
+// before the current chunk is consumed, as the GEMV's tile prefetch does.
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint8_t *buf, unsigned long long bytes,
+                                                              uint32_t *sink)
+{
+    const unsigned long long nchunks = (bytes + kChunk - 1) / kChunk;
+    const unsigned off = threadIdx.x * 16u;
+    auto issue = [&](unsigned long long c, skg::u32x4 (&v)[kUnroll]) {
+        const unsigned long long start = c * kChunk;
+        unsigned len = 0;
+        if (c < nchunks) {
+            const unsigned long long rest = bytes - start;
+            len = (unsigned)(rest < kChunk ? rest : kChunk);
+        }
+        const __amdgpu_buffer_rsrc_t r = skg::make_rsrc(buf + (c < nchunks ? start : 0), len);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            v[u] = skg::load16<NT>(r, off + u * kThreads * 16u);
+    };
+    skg::u32x4 acc = {0u, 0u, 0u, 0u};
+    skg::u32x4 a[kUnroll], b[kUnroll];
+    auto consume = [&](const skg::u32x4 (&v)[kUnroll]) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            acc ^= v[u];
+    };
+    unsigned long long c = blockIdx.x;
+    const unsigned long long step = gridDim.x;
+    if (c < nchunks)
+        issue(c, a);
+    while (c < nchunks) {
+        issue(c + step, b);  // an empty resource past the last chunk: no data moves
+        consume(a);
+        c += step;
+        if (c >= nchunks)
+            break;
+        issue(c + step, a);
+        consume(b);
+        c += step;
+    }
+    sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+}  // namespace
+
+extern "C" size_t skinny_probe_sink_words(int grid_blocks)
+{
+    return grid_blocks > 0 ? (size_t)grid_blocks * kThreads : 0;
+}
+
+extern "C" int skinny_probe_read(const void *buf, size_t bytes, int nontemporal, int grid_blocks,
+                                 uint32_t *sink, hipStream_t stream)
+{
+    if (!sink || grid_blocks < 1 || grid_blocks > 65536 || bytes % 16 != 0 ||
+        (bytes != 0 && !buf) || ((uintptr_t)buf % 16) != 0 || ((uintptr_t)sink % 4) != 0)
+        return -1;
+    const uintptr_t s0 = (uintptr_t)sink, s1 = s0 + skinny_probe_sink_words(grid_blocks) * 4;
+    const uintptr_t b0 = (uintptr_t)buf, b1 = b0 + bytes;
+    if (bytes != 0 && s0 < b1 && b0 < s1)
+        return -1;
+    const uint8_t *p = (const uint8_t *)buf;
+    unsigned long long nbytes = bytes;
+    void *args[] = {&p, &nbytes, &sink};
+    const void *fn = nontemporal ? reinterpret_cast<const void *>(&read_probe_kernel<true>)
+                                 : reinterpret_cast<const void *>(&read_probe_kernel<false>);
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid_blocks), dim3(kThreads), args, 0, stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return -4;
+    }
+    return 0;
+}

@@ -1,0 +1,47 @@
+/* Read-stream probe: the rate at which a plain streaming kernel reads HBM on this
+ * device, the practical ceiling beside which the GEMV's weight stream is judged
+ * (the 8 TB/s peak is a datasheet figure). Measurement only; not part of the GEMM.
+ *
+ * The measured-ceiling comparison follows vLLM PR #65306 (SM90 skinny GEMM plans),
+ * section Validation, which rates the kernels by weight bytes per second against
+ * the memory system; the probe gives the same rate for a kernel that does nothing
+ * but read.
+ *
+ * Library: libskinny_stream_probe.so (built next to libskinny_gemm_bf16.so).
+ */
+#ifndef SKINNY_STREAM_PROBE_H
+#define SKINNY_STREAM_PROBE_H
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Number of sink words a call with this grid writes: grid_blocks * 256. */
+size_t skinny_probe_sink_words(int grid_blocks);
+
+/* Reads `bytes` bytes at device pointer `buf` once, with 16-byte buffer loads
+ * (non-temporal hint if `nontemporal` != 0), in one kernel launch on `stream`.
+ * The buffer is read in 32 KiB chunks, chunk c by block c mod `grid_blocks` (256
+ * threads each), each block loading its next chunk while it consumes the current
+ * one. Every thread XORs the 32-bit words it read into one word and stores it to
+ * sink[b * 256 + thread], so the XOR of all skinny_probe_sink_words(grid_blocks)
+ * sink words equals the XOR of all 32-bit words of the buffer (the check that
+ * every byte was read).
+ *
+ * Arguments: `buf` 16-byte aligned, `bytes` a multiple of 16 (0 allowed: the sink
+ * is written with zeros), `grid_blocks` in 1..65536, `sink` a 4-byte aligned
+ * device buffer of skinny_probe_sink_words(grid_blocks) uint32 words that does not
+ * overlap `buf`. The caller owns both buffers; nothing is allocated.
+ * Returns 0, -1 (invalid argument: nothing enqueued) or -4 (launch failed). */
+int skinny_probe_read(const void *buf, size_t bytes, int nontemporal, int grid_blocks,
+                      uint32_t *sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_STREAM_PROBE_H */

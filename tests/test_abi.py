@@ -30,16 +30,24 @@ def skg():
     return bf16_skinny_gemm_amd
 
 
-def declared_functions():
+PROBE_HEADER = "skinny_stream_probe.h"
+
+
+def declared_functions(headers=None):
+    """Functions declared in include/*.h (or in the named headers only)."""
     names = []
     for fn in sorted(os.listdir(HEADER_DIR)):
-        if not fn.endswith(".h"):
+        if not fn.endswith(".h") or (headers is not None and fn not in headers):
             continue
         text = open(os.path.join(HEADER_DIR, fn)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(skinny_\w+)\s*\(", text, flags=re.M):
             names.append(m.group(1))
     return names
+
+
+def gemm_headers():
+    return [f for f in os.listdir(HEADER_DIR) if f.endswith(".h") and f != PROBE_HEADER]
 
 
 def test_header_declares_entry_points():
@@ -53,8 +61,30 @@ def test_header_declares_entry_points():
 
 def test_library_exports_every_declared_symbol(skg):
     L = skg.lib()
-    for name in declared_functions():
+    for name in declared_functions(gemm_headers()):
         assert hasattr(L, name), f"{name} declared in include/ but not exported"
+
+
+def test_probe_library_exports_and_validates(skg):
+    """The read-stream probe's library exports what its header declares and refuses
+    bad arguments before touching a device."""
+    from bf16_skinny_gemm_amd import probe
+
+    L = probe.lib()
+    names = declared_functions([PROBE_HEADER])
+    assert names == ["skinny_probe_sink_words", "skinny_probe_read"]
+    for name in names:
+        assert hasattr(L, name)
+    assert probe.sink_words(3) == 3 * 256 and probe.sink_words(0) == 0
+    buf, sink = 0x10000000, 0x20000000  # never dereferenced: every call below is refused
+    for args in ((buf, 100, 1, 8, sink),        # bytes not a multiple of 16
+                 (buf, 4096, 1, 0, sink),       # no blocks
+                 (buf, 4096, 1, 65537, sink),   # too many blocks
+                 (buf, 4096, 1, 8, None),       # no sink
+                 (None, 4096, 1, 8, sink),      # no buffer
+                 (buf + 8, 4096, 1, 8, sink),   # misaligned buffer
+                 (buf, 4096, 1, 8, buf + 64)):  # sink inside the buffer
+        assert L.skinny_probe_read(*args, None) == -1, args
 
 
 def test_exports_have_c_linkage(skg):
@@ -66,7 +96,7 @@ def test_exports_have_c_linkage(skg):
     out = subprocess.run(["nm", "-D", "--defined-only", LIB_PATH], capture_output=True,
                          text=True).stdout
     syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
-    for name in declared_functions():
+    for name in declared_functions(gemm_headers()):
         assert name in syms
 
 

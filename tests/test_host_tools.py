@@ -91,6 +91,9 @@ def test_kernel_names_exist_in_the_sources():
 def test_bytes_per_call():
     assert bench.bytes_per_call((4096, 1024, 2)) == 2 * 4096 * 1024 + 2 * 2 * 1024 + 2 * 2 * 4096
     assert bench.bytes_per_call(("pair", 4096, 128, 4)) == 4 * 4096 * 128 + 2 * 4 * 128 + 4 * 4 * 4096
+    assert bench.weight_bytes((4096, 1024, 2)) == 2 * 4096 * 1024
+    assert bench.weight_bytes(("pair", 4096, 128, 4)) == 4 * 4096 * 128
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
 
 
 def test_code_only_digest_ignores_notes():
@@ -145,3 +148,8 @@ def test_refine_twins_add_the_lookahead_form(tmp_path):
     assert [(p.x_in_lds, p.grid_blocks) for p in plans] == [(1, 0)]
     plans = sweep.refine_plans(skg, str(src), 1, 8, 2, False, 1, (0, 256), twins=True)
     assert [(p.x_in_lds, p.grid_blocks) for p in plans] == [(1, 0), (2, 0), (1, 256), (2, 256)]
+
+
+def test_fit_line():
+    a, b = bench.fit_line([1.0, 2.0, 4.0], [3.0, 5.0, 9.0])
+    assert a == pytest.approx(1.0) and b == pytest.approx(2.0)
