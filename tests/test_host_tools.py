@@ -153,3 +153,89 @@ def test_refine_twins_add_the_lookahead_form(tmp_path):
 def test_fit_line():
     a, b = bench.fit_line([1.0, 2.0, 4.0], [3.0, 5.0, 9.0])
     assert a == pytest.approx(1.0) and b == pytest.approx(2.0)
+
+
+def test_parse_grids_refine_tokens():
+    assert sweep.parse_grids("same,balanced,tile") == (sweep.SAME, sweep.BALANCED, sweep.BIG_GRID)
+
+
+def test_rows_per_tile_per_kind():
+    d = _rec(1, 8, 1, 1.0)["plan"]
+    # fixed-K: (4 waves / k_split 2) groups x rows_per_wave 1 x 64/64 rows
+    assert sweep.rows_per_tile(d) == 2
+    assert sweep.rows_per_tile({**d, "lanes_per_row": 16, "rows_per_wave": 2, "k_split": 1}) == 4 * 2 * 4
+    assert sweep.rows_per_tile({**d, "kind": 2, "rows_per_wave": 4, "k_split": 1}) == 16
+    assert sweep.rows_per_tile({**d, "kind": 4, "rows_per_wave": 2, "k_split": 4}) == 8
+    assert sweep.rows_per_tile({**d, "kind": 3}) is None
+
+
+def test_balanced_grids_give_equal_tile_counts():
+    # the KDA in_proj at M = 4: 256 threads, one row per wave -> 4 rows per tile, 3144 tiles
+    d = _rec(12576, 4096, 4, 1.0, k_split=1, chunks=8, grid_blocks=512)["plan"]
+    gs = sweep.balanced_grids(d, 12576)
+    assert gs == [524, 450, 629, 393]
+    tiles = 3144
+    for g in gs:
+        per = -(-tiles // g)
+        # every block but possibly the last one takes exactly `per` tiles
+        assert (g - 1) * per < tiles <= g * per
+    # a pair's grid counts both weights (even blocks serve W0, odd blocks W1)
+    assert sweep.balanced_grids({**d, "grid_blocks": 1024}, 12576, nmats=2) == [2 * g for g in gs]
+    # the nearest to a persistent or per-tile grid are taken around 512
+    assert sweep.balanced_grids({**d, "grid_blocks": 0}, 12576) == gs
+    assert sweep.balanced_grids({**d, "grid_blocks": sweep.BIG_GRID}, 12576) == gs
+    # nothing to balance when every block already has one tile, or for the scalar kind
+    assert sweep.balanced_grids(d, 4) == []
+    assert sweep.balanced_grids({**d, "kind": 3}, 12576) == []
+
+
+def test_rotated_order_moves_every_plan():
+    orders = [sweep.rotated_order(4, r) for r in range(3)]
+    assert orders == [[0, 1, 2, 3], [1, 0, 3, 2], [2, 3, 0, 1]]
+    for o in orders:
+        assert sorted(o) == [0, 1, 2, 3]
+    assert len({o[0] for o in orders}) == 3          # a different plan first each round
+    assert sweep.rotated_order(0, 5) == []
+
+
+def test_refine_same_and_balanced_grids(tmp_path):
+    import bf16_skinny_gemm_amd as skg
+
+    recs = [_rec(12576, 4096, 4, 5.0, grid_blocks=512, chunks=8, k_split=1),
+            _rec(12576, 4096, 4, 5.2, grid_blocks=256, chunks=8, k_split=1),
+            _rec(12576, 4096, 4, 6.0, grid_blocks=0)]
+    a, b = tmp_path / "a.jsonl", tmp_path / "b.jsonl"
+    a.write_text(json.dumps(recs[0]) + "\n" + json.dumps(recs[2]) + "\n")
+    b.write_text(json.dumps(recs[1]) + "\n")
+    plans = sweep.refine_plans(skg, f"{a},{b}", 12576, 4096, 4, False, 1,
+                               (sweep.SAME, sweep.BALANCED))
+    assert [p.grid_blocks for p in plans] == [512, 524, 450, 629, 393]
+    assert all(p.chunks == 8 and p.k_split == 1 for p in plans)
+
+
+def test_emit_inc_uses_stage_two_records_of_a_cell(tmp_path):
+    fast_once = {**_rec(4096, 4096, 1, 6.0, prefetch=1), "stage": 1}
+    final = [{**_rec(4096, 4096, 1, 6.5, prefetch=2), "stage": 2},
+             {**_rec(4096, 4096, 1, 6.6, prefetch=0), "stage": 2}]
+    other = _rec(4096, 4096, 2, 7.0, prefetch=1)                     # unstaged cell
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in [fast_once, *final, other]))
+    out = tmp_path / "plans.inc"
+    sweep.emit_inc(str(src), str(out))
+    rows = re.findall(r"^\{(\d+), (\d+), (\d+), \{([^}]*)\}\},", out.read_text(), re.M)
+    assert [int(v) for v in rows[0][3].split(",")][9] == 2          # not the single-pass 6.0
+    assert [int(v) for v in rows[1][3].split(",")][9] == 1
+
+
+def test_table_plans_reads_the_generated_table(tmp_path):
+    recs = [_rec(4096, 4096, 1, 6.9, grid_blocks=1024, prefetch=2), _rec(2048, 4096, 3, 5.0)]
+    src = tmp_path / "s.jsonl"
+    src.write_text("".join(json.dumps(r) + "\n" for r in recs))
+    out = tmp_path / "plans.inc"
+    sweep.emit_inc(str(src), str(out))
+    got = sweep.table_plans(str(out))
+    assert got == {(2048, 4096, 3): recs[1]["plan"], (4096, 4096, 1): recs[0]["plan"]}
+    # the committed table parses, one plan per (N, K, M), every field present
+    committed = sweep.table_plans()
+    assert len(committed) >= 100
+    assert all(set(p) == set(sweep.PLAN_FIELDS) for p in committed.values())
