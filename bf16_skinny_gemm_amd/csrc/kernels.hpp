@@ -23,12 +23,15 @@
 //  * partial sums of a row meet across its LPR lanes by DPP lane permutations
 //    and row broadcasts, then across the k_split waves of a block in LDS,
 //    always in one fixed order (deterministic results);
-//  * the float32 sum is rounded once to bfloat16, nearest-even, and stored
-//    through a buffer resource over the output row (rows >= N fall outside it).
+//  * the float32 sum is rounded once to bfloat16, nearest-even, and the M x R
+//    results of a lane group are stored together, one store instruction per 16
+//    of them, through a buffer resource over the output (rows >= N never stored).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace skg {
 
@@ -215,28 +218,68 @@ __device__ __forceinline__ void store_out(const Args &a, void *ym, size_t idx, f
         static_cast<uint16_t *>(ym)[idx] = f32_to_bf16(v);
 }
 
-// Output row m of ym (N elements) as a buffer resource: a store to a row >= N,
-// or at offset kOutOfRange, is dropped by the hardware.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const Args &a, void *ym, int m)
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
 {
-    const unsigned eb = a.out_f32 ? 4u : 2u;
-    return make_rsrc(static_cast<char *>(ym) + (size_t)m * a.ldy * eb, (unsigned)a.N * eb);
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
-// Store v as output `row` through the row resource yr if `mine`; otherwise the
-// store is issued with an out-of-range offset and writes nothing. The storing
-// waves of the fast kernels call it from every lane, with no per-lane branch
-// around it (the row bound is the resource's), which measured 1-7% faster per
-// call than lane-predicated global stores behind such branches.
-__device__ __forceinline__ void store_row(const Args &a, __amdgpu_buffer_rsrc_t yr, int row, bool mine,
-                                          float v)
+// In every 16-lane row, lane 15's v moved to lane 15 - S (DPP row_shl:S).
+template <int S>
+__device__ __forceinline__ float from_row_end(float v)
 {
-    if (a.out_f32)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), yr,
-                                              (int)(mine ? (unsigned)row * 4u : kOutOfRange), 0, 0);
+    if constexpr (S == 0)
+        return v;
     else
-        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), yr,
-                                              (int)(mine ? (unsigned)row * 2u : kOutOfRange), 0, 0);
+        return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x100 + S,
+                                                                      0xF, 0xF, false));
+}
+
+// All M output rows of ym as one buffer resource: element (m, n) at m * ldy + n.
+// The host launches the fast kernels only when that span fits in 31 bits.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(const Args &a, void *ym, int M)
+{
+    const unsigned eb = a.out_f32 ? 4u : 2u;
+    return make_rsrc(ym, (unsigned)((M - 1) * a.ldy + a.N) * eb);
+}
+
+// Store the M x R results of a lane group: result k = r * M + m (row m of y,
+// output row row(r)) goes to the lane whose `slot` is k mod SLOTS, and each
+// SLOTS results take one store instruction, issued by every lane with no
+// branch: a lane without a result, or whose row is >= N, passes an offset the
+// hardware drops. val(k, s) is result k as seen from the lane of slot s (after
+// any lane move that takes). One instruction where the rows used to take M x R
+// measured 0.2-0.4 us less per call at M = 4 on the decode shapes.
+template <int M, int R, int SLOTS, typename Val, typename Row>
+__device__ __forceinline__ void store_results(const Args &a, __amdgpu_buffer_rsrc_t yr, int slot, Val &&val,
+                                              Row &&row)
+{
+    constexpr int NV = M * R;
+    static_for<0, (NV + SLOTS - 1) / SLOTS>([&](auto bc) {
+        constexpr int B = decltype(bc)::value;
+        constexpr int NS = NV - B * SLOTS < SLOTS ? NV - B * SLOTS : SLOTS;
+        float v = 0.0f;
+        static_for<0, NS>([&](auto sc) {
+            constexpr int S = decltype(sc)::value;
+            const float u = val(std::integral_constant<int, B * SLOTS + S>{}, sc);
+            v = slot == S ? u : v;
+        });
+        const bool has = slot >= 0 && slot < NS;
+        const int k = has ? B * SLOTS + slot : 0;
+        const int m = k % M;
+        const int rw = row(k / M);
+        const bool mine = has && rw < a.N;
+        const unsigned idx = (unsigned)(m * a.ldy + rw);
+        if (a.out_f32)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), yr,
+                                                  (int)(mine ? idx * 4u : kOutOfRange), 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), yr, (int)(mine ? idx * 2u : kOutOfRange), 0, 0);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -338,10 +381,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     const uint16_t *xm = sc.mat ? a.x1 : a.x;
     void *ym = sc.mat ? a.y1 : a.y0;
-    __amdgpu_buffer_rsrc_t yr[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        yr[m] = out_rsrc(a, ym, m);
+    const __amdgpu_buffer_rsrc_t yr = out_rsrc(a, ym, M);
 
     int it = sc.first;
     int tile = sc.tile(it);
@@ -431,12 +471,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 acc[m][r] = group_sum<LPR>(acc[m][r]);
 
         const int row0 = t * rows_t + grp * ROWS_W;
+        auto row = [&](int r) { return row0 + r * RPI + sub; };
         if constexpr (KW == 1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    store_row(a, yr[m], row0 + r * RPI + sub, kl == OUT, acc[m][r]);
+            if constexpr (LPR >= 32) {
+                // the group's sums sit in its last lane, lane 15 of a 16-lane row
+                store_results<M, R, 16>(a, yr, OUT - kl, [&](auto k, auto s) {
+                    return from_row_end<decltype(s)::value>(acc[k % M][k / M]);
+                }, row);
+            } else {
+                // every lane of the group holds every sum
+                store_results<M, R, LPR>(a, yr, kl, [&](auto k, auto) { return acc[k % M][k / M]; }, row);
+            }
         } else {
             if (kl == OUT) {
 #pragma unroll
@@ -449,16 +494,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
             // the group's first wave sums and stores (a wave-uniform branch: the
             // other waves issue no stores, so nothing delays their loads)
             if (kw == 0) {
+                // every lane of the group reads every sum, one at a time as the
+                // stores take them (a table of all M x R would cost registers)
+                store_results<M, R, (LPR < 16 ? LPR : 16)>(a, yr, kl, [&](auto k, auto) {
+                    constexpr int m = decltype(k)::value % M, r = decltype(k)::value / M;
+                    float s = part[((grp * KW + 0) * M + m) * ROWS_W + r * RPI + sub];
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        float s = part[((grp * KW + 0) * M + m) * ROWS_W + r * RPI + sub];
-#pragma unroll
-                        for (int q = 1; q < KW; ++q)
-                            s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
-                        store_row(a, yr[m], row0 + r * RPI + sub, kl == OUT, s);
-                    }
+                    for (int q = 1; q < KW; ++q)
+                        s += part[((grp * KW + q) * M + m) * ROWS_W + r * RPI + sub];
+                    return s;
+                }, row);
             }
             __syncthreads();
         }
@@ -538,10 +583,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
         return;  // whole block
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
-    __amdgpu_buffer_rsrc_t yr[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        yr[m] = out_rsrc(a, ym, m);
+    const __amdgpu_buffer_rsrc_t yr = out_rsrc(a, ym, M);
 
     {
         const __amdgpu_buffer_rsrc_t xs = make_rsrc(sc.mat ? a.x1 : a.x, x_bytes(a, M));
@@ -599,11 +641,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void loop_k_kernel(Args a, int kpad
             for (int r = 0; r < R; ++r)
                 acc[m][r] = group_sum<64>(acc[m][r]);
 
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int m = 0; m < M; ++m)
-                store_row(a, yr[m], row0 + r, lane == sum_lane<64>(), acc[m][r]);
+        // the sums sit in lane 63, lane 15 of the last 16-lane row
+        store_results<M, R, 16>(a, yr, sum_lane<64>() - lane, [&](auto k, auto s) {
+            return from_row_end<decltype(s)::value>(acc[k % M][k / M]);
+        }, [&](int r) { return row0 + r; });
     }
 }
 
@@ -664,10 +705,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
     const int step = sc.step;
     const uint16_t *wm = sc.mat ? a.w1 : a.w0;
     void *ym = sc.mat ? a.y1 : a.y0;
-    __amdgpu_buffer_rsrc_t yr[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-        yr[m] = out_rsrc(a, ym, m);
+    const __amdgpu_buffer_rsrc_t yr = out_rsrc(a, ym, M);
 
     int it = sc.first;
     int tile = sc.tile(it);
@@ -746,12 +784,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
 #pragma unroll
             for (int m = 0; m < M; ++m)
                 s[r][m] = block_sum(acc[r][m]);
+        // every lane holds the sums of its row lj; block lb stores result lb
+        auto row = [&](int r) { return row0 + r * 4 + lj; };
         if constexpr (KW == 1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < M; ++m)
-                    store_row(a, yr[m], row0 + r * 4 + lj, lb == 0, s[r][m]);
+            store_results<M, R, 16>(a, yr, lb, [&](auto k, auto) { return s[k / M][k % M]; }, row);
         } else {
             if (lb == 0) {
 #pragma unroll
@@ -763,18 +799,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void mfma_kernel(Args a)
             __syncthreads();
             // the group's first wave sums and stores (a wave-uniform branch)
             if (kw == 0) {
+                store_results<M, R, 16>(a, yr, lb, [&](auto k, auto) {
+                    constexpr int m = decltype(k)::value % M, r = decltype(k)::value / M;
+                    float v = part[((grp * KW + 0) * ROWS_W + r * 4 + lj) * M + m];
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const int rr = r * 4 + lj;
-#pragma unroll
-                    for (int m = 0; m < M; ++m) {
-                        float v = part[((grp * KW + 0) * ROWS_W + rr) * M + m];
-#pragma unroll
-                        for (int q = 1; q < KW; ++q)
-                            v += part[((grp * KW + q) * ROWS_W + rr) * M + m];
-                        store_row(a, yr[m], row0 + rr, lb == 0, v);
-                    }
-                }
+                    for (int q = 1; q < KW; ++q)
+                        v += part[((grp * KW + q) * ROWS_W + r * 4 + lj) * M + m];
+                    return v;
+                }, row);
             }
             __syncthreads();
         }

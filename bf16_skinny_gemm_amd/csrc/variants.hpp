@@ -27,7 +27,9 @@ struct Variant {
 
 // Register budget per lane, so that no instance spills: x in registers takes
 // 4*M*CH VGPRs (at most 128), the weight sets in flight 4*R*CH each (two with
-// tile prefetch, one without or with rolling prefetch). Reading x from LDS one
+// tile prefetch, one without or with rolling prefetch), the sums M*R; with x in
+// registers the three may hold 200 between them (the only instances above that,
+// M = 8 with two sets of 2 rows x 4 chunks, spilled). Reading x from LDS one
 // chunk ahead (XL = 2) holds 4*M more and is built for M >= 2 only: at M = 1 a
 // register copy of x is cheaper.
 constexpr bool fits(int M, int CH, int R, int XL, int PF)
@@ -35,7 +37,7 @@ constexpr bool fits(int M, int CH, int R, int XL, int PF)
     const int w = (PF == 1 ? 2 : 1) * R * CH;
     if (XL == 2)
         return M >= 2 && w <= 20;
-    return XL ? w <= 20 : (M * CH <= 32 && M * CH + w <= 48);
+    return XL ? w <= 20 : (M * CH <= 32 && 4 * (M * CH + w) + M * R <= 200);
 }
 
 template <int M, int LPR, int CH, int R, int KW, int XL, bool NT, int PF>

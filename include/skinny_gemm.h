@@ -32,7 +32,8 @@
  *    has 4 rows) with tuned plans for the decode shapes. M > 8 is rejected with
  *    SKINNY_ERR_INVALID_ARG; the caller keeps its general GEMM.
  *  - Fast path: x and W 16-byte aligned, K % 8 == 0 (128-bit weight loads)
- *    and N * (output element bytes) < 2^31. Anything else runs a correct
+ *    and the output span ((M - 1) * ldy + N) * (output element bytes) < 2^31,
+ *    where ldy = N except for the strided pair. Anything else runs a correct
  *    element-wise path; it is not an error (an explicit plan that cannot run
  *    returns SKINNY_ERR_INVALID_ARG or SKINNY_ERR_UNSUPPORTED instead).
  *  - Errors are returned, never raised or aborted: arguments are validated

@@ -750,3 +750,41 @@ def test_pair_strided_odd_stride_and_guard(skg):
     torch.cuda.synchronize()
     assert torch.all(o0.view(torch.int16) == 0) and torch.all(o1.view(torch.int16) == 0)
     assert torch.all(big[:, N:N + 7] == -3.0) and torch.all(big[:, 2 * N + 7:] == -3.0)
+
+
+def test_output_span_limits(skg):
+    """The kernels store all M output rows through one buffer resource, so the span
+    ((M - 1) * ldy + N) * 2 bytes must stay below 2^31. Just below it (rows 2^30 - N - 1
+    elements apart) the fast kernels write near the top of the range; just above it
+    (2^30 apart) the tuned plan is refused and the default call takes the
+    element-wise path. Both must leave the columns between the outputs untouched."""
+    M, N, K = 2, 300, 128
+    free, _ = torch.cuda.mem_get_info()
+    if free < 8 * 2 ** 30:
+        pytest.skip("not enough device memory")
+    xm, W0, W1 = _merged_case(M, N, K, seed=140)
+    xmd, W0d, W1d = to_dev(xm), to_dev(W0), to_dev(W1)
+    x0 = np.ascontiguousarray(xm[:, :K])
+    x1 = np.ascontiguousarray(xm[:, K:])
+    plan, tuned = skg.skinny_gemm_get_plan(N, K, M)
+    buf = torch.empty((1 << 30) + 4 * N, dtype=torch.bfloat16, device="cuda")
+    for ldy, fast in (((1 << 30) - N - 1, True), (1 << 30, False)):
+        buf[:4 * N].fill_(-3.0)
+        buf[ldy:ldy + 4 * N].fill_(-3.0)
+        o0 = torch.as_strided(buf, (M, N), (ldy, 1), 0)
+        o1 = torch.as_strided(buf, (M, N), (ldy, 1), 2 * N)
+        if fast:
+            skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], W0d, W1d, out0=o0, out1=o1, plan=plan)
+        else:
+            with pytest.raises(skg.SkinnyError) as e:
+                skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], W0d, W1d, out0=o0, out1=o1, plan=plan)
+            assert e.value.status == skg.SKINNY_ERR_UNSUPPORTED
+            skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], W0d, W1d, out0=o0, out1=o1)
+        torch.cuda.synchronize()
+        check(o0.contiguous(), x0, W0, label=f"span y0 ldy={ldy}")
+        check(o1.contiguous(), x1, W1, label=f"span y1 ldy={ldy}")
+        for base in (0, ldy):
+            assert torch.all(buf[base + N:base + 2 * N] == -3.0)
+            assert torch.all(buf[base + 3 * N:base + 4 * N] == -3.0)
+    del buf
+    torch.cuda.empty_cache()
