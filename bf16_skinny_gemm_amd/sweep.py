@@ -384,15 +384,20 @@ def pick(records, tol=0.005):
 
 
 def emit_inc(paths, out=INC_PATH):
-    """Write the plan table from one or more sweep files (all records pooled)."""
+    """Write the plan table from one or more sweep files. A cell's records come
+    from the last file in the list that holds the cell, so a later pass over
+    some cells (timed on one box, in the same rounds) replaces the earlier one
+    for those cells without mixing timings from different runs."""
     recs = {}
     for path in paths.split(","):
+        mine = {}
         with open(path) as f:
             for line in f:
                 r = json.loads(line)
                 if "plan" not in r:
                     continue
-                recs.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+                mine.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+        recs.update(mine)
     for key, rs in recs.items():
         # a cell re-timed in rounds is decided by those records alone
         if any(r.get("stage") == 2 for r in rs):

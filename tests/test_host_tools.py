@@ -239,3 +239,16 @@ def test_table_plans_reads_the_generated_table(tmp_path):
     committed = sweep.table_plans()
     assert len(committed) >= 100
     assert all(set(p) == set(sweep.PLAN_FIELDS) for p in committed.values())
+
+
+def test_emit_inc_takes_each_cell_from_the_last_file_holding_it(tmp_path):
+    first = [_rec(4096, 4096, 1, 6.0, prefetch=1), _rec(4096, 4096, 2, 7.0, prefetch=1)]
+    later = [_rec(4096, 4096, 2, 7.3, prefetch=2)]                  # slower, but a later pass
+    a, b = tmp_path / "a.jsonl", tmp_path / "b.jsonl"
+    a.write_text("".join(json.dumps(r) + "\n" for r in first))
+    b.write_text("".join(json.dumps(r) + "\n" for r in later))
+    out = tmp_path / "plans.inc"
+    sweep.emit_inc(f"{a},{b}", str(out))
+    got = sweep.table_plans(str(out))
+    assert got[(4096, 4096, 1)]["prefetch"] == 1                    # only in the first file
+    assert got[(4096, 4096, 2)]["prefetch"] == 2                    # the later file decides
