@@ -440,8 +440,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             if constexpr (XL == 2) {
-                if (j + 1 < CH)
+                if (j + 1 < CH) {
                     read_x(j + 1, xn);
+                    // keep these reads ahead of chunk j's products: left alone, the
+                    // scheduler sinks them below most of the chunk, and chunk j+1 then
+                    // starts by waiting out the LDS latency
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
 #pragma unroll
             for (int m = 0; m < M; ++m) {
