@@ -413,6 +413,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 xr[m][j] = load16<false>(xs, (unsigned)(m * ldx + (int)kbase + j * LPR * 8) * 2u);
     }
 
+    // With x read one chunk ahead (XL = 2), chunk 0's pieces stay in registers for
+    // every tile (x is the same for all of them): re-read at each tile start, they
+    // waited behind the tile's first weights.
+    u32x4 x0[XL == 2 ? M : 1];
+    if constexpr (XL == 2) {
+        const volatile __attribute__((address_space(3))) u32x4 *xp0 =
+            (const volatile __attribute__((address_space(3))) u32x4 *)x_lds;
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+            x0[m] = xp0[(m * K + (int)kbase) / 8];
+    }
+
     // Multiply tile t's weights wv, reduce and store; after_chunk(j) runs once
     // chunk j of wv is no longer needed.
     auto consume = [&](int t, const u32x4 (&wv)[R][CH], auto &&after_chunk) {
@@ -435,8 +447,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
             for (int m = 0; m < (XL == 2 ? M : 1); ++m)
                 dst[m] = xp[(m * K + (int)kbase + j * LPR * 8) / 8];
         };
-        if constexpr (XL == 2)
-            read_x(0, xc);
+        if constexpr (XL == 2) {
+#pragma unroll
+            for (int m = 0; m < M; ++m)
+                xc[m] = x0[m];
+        }
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             if constexpr (XL == 2) {
