@@ -413,11 +413,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 xr[m][j] = load16<false>(xs, (unsigned)(m * ldx + (int)kbase + j * LPR * 8) * 2u);
     }
 
-    // With x read one chunk ahead (XL = 2), chunk 0's pieces stay in registers for
-    // every tile (x is the same for all of them): re-read at each tile start, they
-    // waited behind the tile's first weights.
-    u32x4 x0[XL == 2 ? M : 1];
-    if constexpr (XL == 2) {
+    // With x in LDS, chunk 0's pieces stay in registers for every tile (x is the
+    // same for all of them): re-read at each tile start, they waited behind the
+    // tile's first weights.
+    u32x4 x0[XL ? M : 1];
+    if constexpr (XL) {
         const volatile __attribute__((address_space(3))) u32x4 *xp0 =
             (const volatile __attribute__((address_space(3))) u32x4 *)x_lds;
 #pragma unroll
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void fixed_k_kernel(Args a)
                 if constexpr (XL == 2)
                     xv = xc[m];
                 else if constexpr (XL == 1)
-                    xv = xp[(m * K + (int)kbase + j * LPR * 8) / 8];
+                    xv = j == 0 ? x0[m] : xp[(m * K + (int)kbase + j * LPR * 8) / 8];
                 else
                     xv = xr[m][j];
 #pragma unroll
