@@ -307,12 +307,16 @@ def gemm_pair(x: torch.Tensor, W0: torch.Tensor, W1: torch.Tensor,
     if tuple(W0.shape) != tuple(W1.shape) or W0.shape[1] != K:
         raise ValueError(f"shapes: x {tuple(x.shape)}, W0 {tuple(W0.shape)}, W1 {tuple(W1.shape)}")
     N = W0.shape[0]
+    if W0.device != x.device or W1.device != x.device:
+        raise ValueError("x, W0 and W1 must be on the same device")
     outs = []
     for o, name in ((out0, "out0"), (out1, "out1")):
         if o is None:
             o = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
         else:
             _check_tensor(o, name)
+            if o.device != x.device:
+                raise ValueError(f"{name} must be on {x.device}")
             if tuple(o.shape) != (M, N):
                 raise ValueError(f"{name} must be [{M}, {N}]")
         outs.append(o)
@@ -351,6 +355,8 @@ def gemm_pair_strided(x0: torch.Tensor, x1: torch.Tensor, W0: torch.Tensor, W1: 
     if tuple(W0.shape) != tuple(W1.shape) or W0.shape[1] != K:
         raise ValueError(f"shapes: x {tuple(x0.shape)}, W0 {tuple(W0.shape)}, W1 {tuple(W1.shape)}")
     N = W0.shape[0]
+    if x1.device != x0.device or W0.device != x0.device or W1.device != x0.device:
+        raise ValueError("x0, x1, W0 and W1 must be on the same device")
     if out0 is None and out1 is None:
         merged = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=x0.device)
         out0, out1 = merged[:, :N], merged[:, N:]
@@ -358,6 +364,8 @@ def gemm_pair_strided(x0: torch.Tensor, x1: torch.Tensor, W0: torch.Tensor, W1: 
         raise ValueError("give both out0 and out1, or neither")
     for o, name in ((out0, "out0"), (out1, "out1")):
         _check_rowview(o, name)
+        if o.device != x0.device:
+            raise ValueError(f"{name} must be on {x0.device}")
         if tuple(o.shape) != (M, N):
             raise ValueError(f"{name} must be [{M}, {N}]")
     if out0.stride(0) != out1.stride(0):

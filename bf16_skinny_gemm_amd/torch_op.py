@@ -50,6 +50,10 @@ def qualifies(x: torch.Tensor, weight: torch.Tensor, bias: torch.Tensor | None =
         return False
     if weight.dim() != 2 or x.dim() < 1 or x.shape[-1] != weight.shape[1]:
         return False
+    if not weight.is_contiguous():
+        # a strided weight would have to be copied whole on every call (634 MB for
+        # the LM head): leave it to the standard path
+        return False
     m = 1
     for d in x.shape[:-1]:
         m *= d
@@ -70,12 +74,11 @@ def linear(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
     x2 = x.reshape(-1, K)
     if not x2.is_contiguous():
         x2 = x2.contiguous()
-    w = weight if weight.is_contiguous() else weight.contiguous()
     y = torch.empty((*x.shape[:-1], N), dtype=torch.bfloat16, device=x.device)
     # qualifies() has checked dtypes, devices and shapes: call the C entry point
     # directly (it raises if the library is missing or refuses the call)
     with _on_device(x.device):
-        skinny_gemm_bf16(x2.data_ptr(), w.data_ptr(), y.data_ptr(), x2.shape[0], N, K,
+        skinny_gemm_bf16(x2.data_ptr(), weight.data_ptr(), y.data_ptr(), x2.shape[0], N, K,
                          _stream_handle(x.device))
     return y
 

@@ -121,3 +121,19 @@ def test_op_under_graph_capture(op):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_strided_weight_is_not_routed(op):
+    """A non-contiguous weight would need a whole copy per call: it stays on F.linear."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.manual_seed(1)
+    wt = torch.randn(512, 256, device="cuda").to(torch.bfloat16)
+    w = wt.t()  # [256, 512] view with strides (1, 256)
+    x = torch.randn(2, 512, device="cuda").to(torch.bfloat16)
+    assert not w.is_contiguous()
+    assert not op.qualifies(x, w)
+    assert torch.equal(op.skinny_linear(x, w), torch.nn.functional.linear(x, w))
+    with pytest.raises(ValueError):
+        torch.ops.skinny.linear(x, w)
