@@ -9,11 +9,9 @@
 #include "skinny_gemm.h"
 
 #include "kernels.hpp"
+#include "validate.hpp"
 
 namespace skg_host {
-
-// Largest token count M the kernels are compiled for.
-constexpr int kMaxM = 8;
 
 // A compiled variant: the plan fields that select template instances, one
 // kernel per M (NULL where that M would not fit the register budget, or for the

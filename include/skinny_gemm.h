@@ -47,7 +47,9 @@
  *  - Thread safety: every entry point may be called from any host thread; the
  *    only shared state is host-side caches filled on first use under a lock or
  *    with atomics (device properties; per kernel, its occupancy, static LDS
- *    size and raised LDS limit).
+ *    size and raised LDS limit; per (device, N, K, M, single or pair), the
+ *    resolved launch of the default plan, written once and then read without
+ *    a lock, so that a repeated call does no table lookup).
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H

@@ -40,6 +40,31 @@ size_t skinny_probe_sink_words(int grid_blocks);
 int skinny_probe_read(const void *buf, size_t bytes, int nontemporal, int grid_blocks,
                       uint32_t *sink, hipStream_t stream);
 
+/* Sink words skinny_probe_read_tiles writes for this buffer size and shape: one
+ * per wave, ceil(bytes / tile) * threads / 64 with tile = threads / 64 * loads KiB;
+ * 0 for a shape it refuses. */
+size_t skinny_probe_tiles_sink_words(size_t bytes, int loads, int threads);
+
+/* Reads `bytes` bytes at `buf` once, one block of `threads` threads per tile of
+ * threads / 64 * `loads` KiB, with the load schedule of the GEMV's one-block-per-
+ * tile plans at M = 1: each wave issues `loads` 16-byte-per-lane loads over
+ * `loads` consecutive KiB before consuming any (non-temporal hint if
+ * `nontemporal` != 0). Each wave stores the XOR of the 32-bit words it read to its
+ * own sink word, so the XOR of all skinny_probe_tiles_sink_words() words equals
+ * the XOR of the buffer's words. A ragged last tile reads zeros past the end.
+ *
+ * Arguments: `loads` 2, 4, 8 or 16; `threads` a multiple of 64 in 64..1024;
+ * `buf` 16-byte aligned and non-null; `bytes` a positive multiple of 16; `sink`
+ * 4-byte aligned, skinny_probe_tiles_sink_words() words, not overlapping `buf`.
+ * Returns 0, -1 (invalid argument: nothing enqueued) or -4 (launch failed). */
+int skinny_probe_read_tiles(const void *buf, size_t bytes, int nontemporal, int loads, int threads,
+                            uint32_t *sink, hipStream_t stream);
+
+/* Launches a kernel that does nothing, `grid_blocks` (1..2^24) blocks of `threads`
+ * (a multiple of 64 in 64..1024): the per-launch floor under graph replay.
+ * Returns 0, -1 (invalid argument) or -4 (launch failed). */
+int skinny_probe_empty(int grid_blocks, int threads, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,7 @@ __all__ = [
     "scaled_activations",
     "sparse_activations",
     "small_int_bf16",
+    "device_weights",
     "BF16_ONE",
 ]
 
@@ -108,3 +109,22 @@ def small_int_bf16(shape, lo: int, hi: int, g: np.random.Generator) -> np.ndarra
     """Uniform integers in [lo, hi] as bf16 bits (exact for |v| <= 256)."""
     a = g.integers(lo, hi + 1, size=shape).astype(np.float32)
     return f32_to_bf16_bits(a)
+
+
+def device_weights(N: int, K: int, seed: int, tensor_id: int, device):
+    """W[N, K] ~ N(0, 1/K) drawn on the GPU, as a bfloat16 torch tensor.
+
+    For the decode-step chain, whose 186 distinct weights (7.5 GB) would take
+    minutes through numpy: torch's Philox generator on `device`, seeded with
+    ``seed * 1_000_003 + tensor_id``, draws float32 standard normals, they are
+    scaled by 1/sqrt(K) in float32 and rounded to bfloat16 by torch's
+    nearest-even conversion. The same bits serve both sides: the oracle reads a
+    host copy of the tensor, the kernels the tensor itself.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(tensor_id))
+    a = torch.randn((N, K), generator=g, device=device, dtype=torch.float32)
+    a.mul_(float(np.float32(1.0 / np.sqrt(K))))
+    return a.to(torch.bfloat16)

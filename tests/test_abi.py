@@ -72,7 +72,8 @@ def test_probe_library_exports_and_validates(skg):
 
     L = probe.lib()
     names = declared_functions([PROBE_HEADER])
-    assert names == ["skinny_probe_sink_words", "skinny_probe_read"]
+    assert names == ["skinny_probe_sink_words", "skinny_probe_read", "skinny_probe_tiles_sink_words",
+                     "skinny_probe_read_tiles", "skinny_probe_empty"]
     for name in names:
         assert hasattr(L, name)
     assert probe.sink_words(3) == 3 * 256 and probe.sink_words(0) == 0
@@ -85,6 +86,22 @@ def test_probe_library_exports_and_validates(skg):
                  (buf + 8, 4096, 1, 8, sink),   # misaligned buffer
                  (buf, 4096, 1, 8, buf + 64)):  # sink inside the buffer
         assert L.skinny_probe_read(*args, None) == -1, args
+    # the one-block-per-tile reader: one sink word per wave, refused shapes give 0 words
+    assert probe.tiles_sink_words(1 << 20, 4, 256) == (1 << 20) // (16 << 10) * 4
+    assert probe.tiles_sink_words((1 << 20) + 16, 4, 256) == ((1 << 20) // (16 << 10) + 1) * 4
+    assert probe.tiles_sink_words(4096, 3, 256) == 0 and probe.tiles_sink_words(4096, 4, 96) == 0
+    for args in ((buf, 100, 1, 4, 256, sink),        # bytes not a multiple of 16
+                 (buf, 0, 1, 4, 256, sink),          # nothing to read
+                 (buf, 4096, 1, 5, 256, sink),       # loads not 2, 4, 8 or 16
+                 (buf, 4096, 1, 4, 100, sink),       # threads not a multiple of 64
+                 (buf, 4096, 1, 4, 2048, sink),      # too many threads
+                 (buf, 4096, 1, 4, 256, None),       # no sink
+                 (None, 4096, 1, 4, 256, sink),      # no buffer
+                 (buf + 8, 4096, 1, 4, 256, sink),   # misaligned buffer
+                 (buf, 4096, 1, 4, 256, buf + 64)):  # sink inside the buffer
+        assert L.skinny_probe_read_tiles(*args, None) == -1, args
+    for grid, threads in ((0, 256), (1 << 25, 256), (8, 32), (8, 2048), (8, 100)):
+        assert L.skinny_probe_empty(grid, threads, None) == -1, (grid, threads)
 
 
 def test_exports_have_c_linkage(skg):
@@ -314,3 +331,20 @@ def test_pair_strided_validation(skg):
     ok = (x0, x1, 2 * K, W, W1, y0, y0 + 2 * N, 2 * N, M, N, K)
     if not __import__("torch").cuda.is_available():
         assert L.skinny_gemm_bf16_pair_strided(*ok, None) == skg.SKINNY_ERR_UNSUPPORTED
+
+
+def test_plan_table_covers_the_decode_shapes():
+    """The generated table holds rows for M = 1..8 of every decode shape (the
+    configurations' shapes, the paired (4096,128) and (2048,128), the router gate,
+    the merged f_a/g_a and the TP4/TP8 rank shapes); the GPU parity suite runs
+    each of them at full size."""
+    path = os.path.join(ROOT, "bf16_skinny_gemm_amd", "csrc", "plans_gfx950.inc")
+    cells = {}
+    for n, k, m in re.findall(r"^\{(\d+), (\d+), (\d+), \{", open(path).read(), re.M):
+        cells.setdefault((int(n), int(k)), set()).add(int(m))
+    want = [(4096, 1024), (12576, 4096), (4096, 4096), (2048, 4096), (8192, 1536), (4096, 8192),
+            (77440, 4096), (4096, 128), (2048, 128), (288, 4096), (256, 4096), (6416, 4096),
+            (19360, 4096), (38720, 4096)]
+    assert sorted(cells) == sorted(want)
+    for s in want:
+        assert cells[s] == set(range(1, 9)), s

@@ -153,31 +153,75 @@ def test_block_sizes_and_persistent_grid(skg, tpb):
 # the decode shapes at full size through the default entry point
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("shape", CONFIG_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
-def test_config_shapes_full(skg, shape):
+def table_shapes():
+    """Every (N, K) of the generated plan table, with the token counts it tunes."""
+    import os
+    import re
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "bf16_skinny_gemm_amd", "csrc", "plans_gfx950.inc")
+    cells = {}
+    for n, k, m in re.findall(r"^\{(\d+), (\d+), (\d+), \{", open(path).read(), re.M):
+        cells.setdefault((int(n), int(k)), []).append(int(m))
+    return sorted(cells.items())
+
+
+@pytest.mark.parametrize("shape,ms", [pytest.param(s, m, id=f"{s[0]}x{s[1]}")
+                                      for s, m in table_shapes() if s != LM_HEAD])
+def test_table_shapes_full(skg, shape, ms):
+    """Every (N, K, M) the plan table tunes, at its full size through the default
+    entry point (the table's plan, its grid), the whole output against the oracle:
+    G1 per element, G2 per row, S1. The K = 128 shapes are the paired projections'
+    and also run as pairs."""
     N, K = shape
+    assert sorted(ms) == list(range(1, 9)), f"table rows of {shape}: {ms}"
     W = synth.weights(N, K, seed=0, shape_id=N * 7 + K, tensor_id=1)
     Wd = to_dev(W)
-    for M in range(1, 9):
+    W1 = W1d = None
+    if K == 128:
+        W1 = synth.weights(N, K, seed=0, shape_id=N * 7 + K, tensor_id=2)
+        W1d = to_dev(W1)
+    for M in ms:
         x = synth.activations(M, K, seed=0, shape_id=N * 7 + K, tensor_id=0)
-        y = skg.gemm(to_dev(x), Wd)
+        xd = to_dev(x)
+        plan, tuned = skg.skinny_gemm_get_plan(N, K, M)
+        assert tuned, f"({N},{K}) M={M} has no table row"
+        y = skg.gemm(xd, Wd)
         torch.cuda.synchronize()
-        check(y, x, W, label=f"N={N} K={K} M={M}")
+        check(y, x, W, label=f"N={N} K={K} M={M} {plan}")
+        if W1 is not None:
+            y0, y1 = skg.gemm_pair(xd, Wd, W1d)
+            torch.cuda.synchronize()
+            check(y0, x, W, label=f"pair y0 N={N} K={K} M={M}")
+            check(y1, x, W1, label=f"pair y1 N={N} K={K} M={M}")
 
 
-def test_lm_head_sampled(skg):
-    """(77440, 4096): full-size launch, oracle on the first and last tiles plus random rows."""
+@pytest.mark.parametrize("M", range(1, 9))
+def test_lm_head_full(skg, M):
+    """(77440, 4096), 634 MB: the whole output of every row against the oracle,
+    G1 per element, G2 (cosine >= 0.99999) per output row, S1."""
     N, K = LM_HEAD
-    W = synth.weights(N, K, seed=0, shape_id=5, tensor_id=1)
-    Wd = to_dev(W)
-    g = np.random.default_rng(3)
-    rows = np.unique(np.concatenate([np.arange(0, 256), np.arange(N - 256, N),
-                                     g.integers(0, N, 4096)])).astype(np.int64)
-    for M in (1, 2, 4, 8):
-        x = synth.activations(M, K, seed=0, shape_id=5, tensor_id=0)
-        y = skg.gemm(to_dev(x), Wd)
-        torch.cuda.synchronize()
-        check(y, x, W, rows=rows, label=f"lm_head M={M}")
+    W = _lm_head_weight()
+    x = synth.activations(M, K, seed=0, shape_id=5, tensor_id=0)
+    y = skg.gemm(to_dev(x), _lm_head_weight_dev())
+    torch.cuda.synchronize()
+    res = check(y, x, W, label=f"lm_head M={M}")
+    assert res["min_cos"] >= 0.99999 and res["n"] == M * N
+
+
+_LM = {}
+
+
+def _lm_head_weight():
+    if "host" not in _LM:
+        _LM["host"] = synth.weights(*LM_HEAD, seed=0, shape_id=5, tensor_id=1)
+    return _LM["host"]
+
+
+def _lm_head_weight_dev():
+    if "dev" not in _LM:
+        _LM["dev"] = to_dev(_lm_head_weight())
+    return _LM["dev"]
 
 
 def test_pair_shape(skg):

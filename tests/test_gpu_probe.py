@@ -27,6 +27,26 @@ def test_probe_reads_every_byte(nbytes, grid, nt):
     assert np.all(got[probe.sink_words(grid):] == 0xFFFFFFFF)   # nothing written past the sink
 
 
+@pytest.mark.parametrize("nbytes,loads,threads,nt", [(16, 2, 64, 1), (4096, 4, 256, 0),
+                                                     ((1 << 20) + 48, 4, 256, 1),
+                                                     ((3 << 20) + 1024, 8, 512, 0),
+                                                     (64 << 20, 16, 128, 1), (64 << 20, 4, 1024, 1)])
+def test_tile_probe_reads_every_byte(nbytes, loads, threads, nt):
+    from bf16_skinny_gemm_amd import probe
+
+    host = np.random.default_rng([nbytes, loads, threads]).integers(0, 1 << 32, nbytes // 4,
+                                                                   dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).to("cuda")
+    words = probe.tiles_sink_words(nbytes, loads, threads)
+    sink = torch.full((words + 64,), -1, dtype=torch.int32, device="cuda")
+    probe.read_tiles(buf, sink, loads=loads, threads=threads, nontemporal=bool(nt))
+    probe.empty(64, 256)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    assert np.bitwise_xor.reduce(got[:words]) == np.bitwise_xor.reduce(host)
+    assert np.all(got[words:] == 0xFFFFFFFF)   # nothing written past the sink
+
+
 def test_probe_rejects_bad_sink():
     from bf16_skinny_gemm_amd import probe
 

@@ -252,3 +252,48 @@ def test_emit_inc_takes_each_cell_from_the_last_file_holding_it(tmp_path):
     got = sweep.table_plans(str(out))
     assert got[(4096, 4096, 1)]["prefetch"] == 1                    # only in the first file
     assert got[(4096, 4096, 2)]["prefetch"] == 2                    # the later file decides
+
+
+def test_split_trace_cuts_at_markers():
+    mk = "skg::zero_kernel(void*, void*, int, int, long long, int)"
+    k1 = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, 0, true, 1>(skg::Args)"
+    pr = "void (anonymous namespace)::read_tiles_kernel<4, true>(unsigned char const*, unsigned long long, unsigned int*)"
+    rows = [(0, 5, "at::native::fill"),                     # before the first marker: ignored
+            (10, 11, mk), (20, 23000, k1), (30, 33000, k1),
+            (40, 41, mk), (50, 52000, pr), (55, 56, "at::native::copy"),  # torch kernels ignored
+            (60, 61, mk), (70, 71000, k1)]                  # wrong count: left out
+    got = bench.split_trace(rows, [("a", 2), ("b", 1), ("c", 2)])
+    assert got == {"a": [22.98, 32.97], "b": [51.95]}
+
+
+def test_expected_trace_units_match_the_groups():
+    args = bench.parse([])
+    units = bench.expected_trace_units(args)
+    names = [n for n, _ in units]
+    assert names[:2] == ["chain:M1", "chain:M4"]
+    assert dict(units)["chain:M1"] == 186 * bench.TRACE_REPLAYS["chain"]
+    # every cell at M = 1, 2, 4, and a dependent chain where N >= K
+    assert "cell:(77440,4096)M4" in names and "dep:(77440,4096)M4" in names
+    assert "cell:(2048,4096)M1" in names and "dep:(2048,4096)M1" not in names
+    assert "dep:pair2x(4096,128)M2" in names
+    # copies per cell: >= 1 GiB of rotation
+    assert dict(units)["cell:(4096,1024)M1"] == 128 * bench.TRACE_REPLAYS["cell"]
+    assert dict(units)["cell:(77440,4096)M1"] == 2 * bench.TRACE_REPLAYS["cell"]
+    assert sum(1 for n in names if n.startswith("probe:")) == 8 * len(bench.PROBE_SHAPES)
+    assert [n for n in names if n.startswith("empty:")] == [f"empty:{g}" for g in bench.EMPTY_GRIDS]
+    lean = bench.expected_trace_units(bench.parse(["--no-cells", "--no-probe", "--chain-ms", "1"]))
+    assert lean == [("chain:M1", 186 * bench.TRACE_REPLAYS["chain"])]
+    kda = bench.expected_trace_units(bench.parse(["--workload", "kda", "--no-dependent", "--no-probe"]))
+    assert [n for n, _ in kda] == [f"cell:({n},4096)M{m}" for n in (12576, 4096) for m in (1, 2, 4)]
+
+
+def test_chain_matches_the_decode_step():
+    assert sum(n for _, _, n in bench.CHAIN) == 186 == len(bench.CHAIN_CALLS)
+    assert abs(bench.chain_bytes(1) / 1e9 - 7.53) < 0.01
+
+
+def test_read_kernel_trace_orders_by_start(tmp_path):
+    p = tmp_path / "x_kernel_trace.csv"
+    p.write_text("Kind,Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
+                 "KERNEL_DISPATCH,2,b,200,300\nKERNEL_DISPATCH,1,a,100,150\n")
+    assert bench.read_kernel_trace([str(p)]) == [(100, 150, "a"), (200, 300, "b")]
