@@ -552,11 +552,15 @@ def trace_pass(args) -> int:
     for gname, units, _ in unit_groups(ctx, cells, with_chain, False, not args.no_dependent,
                                        not args.no_probe):
         for u in units:
+            # a marker on each side: whatever runs between units (the next group's
+            # eager warm-ups) falls between a closing and an opening marker
             torch.cuda.synchronize()
-            ctx.skg.gemm(xm, wm, out=ym)  # marker
+            ctx.skg.gemm(xm, wm, out=ym)
             torch.cuda.synchronize()
             for _ in range(TRACE_REPLAYS[u.kind]):
                 u.graph.replay()
+            torch.cuda.synchronize()
+            ctx.skg.gemm(xm, wm, out=ym)
             torch.cuda.synchronize()
             n += 1
         log(f"trace pass: {gname} done ({n} units)")
@@ -587,10 +591,12 @@ def read_kernel_trace(paths):
 
 
 def split_trace(rows, expected):
-    """Cut a launch-ordered trace at the marker dispatches. `expected` lists
+    """Cut a launch-ordered trace at the marker dispatches. Each unit's replays
+    sit between an opening and a closing marker, so the stretches between
+    markers alternate: unit, gap (other work), unit, gap, ... `expected` lists
     (unit name, dispatches) in the order the units were replayed. Returns
     {unit name: [duration_us of each of its dispatches, in order]}, leaving out a
-    unit whose segment does not hold exactly the dispatches expected."""
+    unit whose stretch does not hold exactly the dispatches expected."""
     segs, cur = [], None
     for (t0, t1, name) in rows:
         if MARKER in name:
@@ -599,7 +605,7 @@ def split_trace(rows, expected):
         elif cur is not None and any(k in name for k in TRACED_KERNELS):
             cur.append((t1 - t0) / 1000.0)
     out = {}
-    for (uname, count), seg in zip(expected, segs):
+    for (uname, count), seg in zip(expected, segs[0::2]):
         if len(seg) == count:
             out[uname] = seg
     return out

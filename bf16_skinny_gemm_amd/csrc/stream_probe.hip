@@ -63,6 +63,13 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const uint8_t *buf
     sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// v ^ (v of the lane the DPP control names); rows outside ROW_MASK take 0 and keep v.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ unsigned dpp_xor(unsigned v)
+{
+    return v ^ (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
 // One block per tile: block b reads bytes [b*T, (b+1)*T) of the buffer, T = waves
 // * LOADS KiB. Wave w of the block takes LOADS consecutive KiB, each one 16-byte
 // load per lane (1 KiB per instruction), all issued before any is consumed: the
@@ -89,11 +96,17 @@ __global__ __launch_bounds__(1024) void read_tiles_kernel(const uint8_t *buf, un
 #pragma unroll
     for (int u = 0; u < LOADS; ++u)
         acc ^= v[u];
+    // XOR across the wave with DPP moves (the butterfly the GEMV's row sums take),
+    // so a wave retires as soon after its last load as the GEMV's do; lane 63
+    // ends with the wave's XOR
     unsigned w = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-        w ^= (unsigned)__shfl_xor((int)w, d);
-    if (lane == 0)
+    w = dpp_xor<0xB1>(w);       // quad_perm [1,0,3,2]
+    w = dpp_xor<0x4E>(w);       // quad_perm [2,3,0,1]
+    w = dpp_xor<0x141>(w);      // row_half_mirror
+    w = dpp_xor<0x140>(w);      // row_mirror
+    w = dpp_xor<0x142, 0xA>(w); // row_bcast:15 into rows 1 and 3
+    w = dpp_xor<0x143, 0xC>(w); // row_bcast:31 into rows 2 and 3
+    if (lane == 63)
         sink[(size_t)blockIdx.x * waves + wave] = w;
 }
 

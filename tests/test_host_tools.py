@@ -259,9 +259,11 @@ def test_split_trace_cuts_at_markers():
     k1 = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, 0, true, 1>(skg::Args)"
     pr = "void (anonymous namespace)::read_tiles_kernel<4, true>(unsigned char const*, unsigned long long, unsigned int*)"
     rows = [(0, 5, "at::native::fill"),                     # before the first marker: ignored
-            (10, 11, mk), (20, 23000, k1), (30, 33000, k1),
+            (10, 11, mk), (20, 23000, k1), (30, 33000, k1), (35, 36, mk),
+            (37, 38000, k1),                                # between units (a warm-up): ignored
             (40, 41, mk), (50, 52000, pr), (55, 56, "at::native::copy"),  # torch kernels ignored
-            (60, 61, mk), (70, 71000, k1)]                  # wrong count: left out
+            (57, 58, mk),
+            (60, 61, mk), (70, 71000, k1), (75, 76, mk)]    # wrong count: left out
     got = bench.split_trace(rows, [("a", 2), ("b", 1), ("c", 2)])
     assert got == {"a": [22.98, 32.97], "b": [51.95]}
 
