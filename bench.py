@@ -106,7 +106,9 @@ def parse(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300, help="timed replays of the step")
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="chain", choices=["chain"] + sorted(CELL_WORKLOADS))
+    ap.add_argument("--workload", default="chain", choices=["chain", "cells"] + sorted(CELL_WORKLOADS))
+    ap.add_argument("--only", help="cells workload: shapes to run, e.g. 4096x4096,2048x4096 or pair4096x128")
+    ap.add_argument("--ms", default="1,2,4", help="cells workload: token counts")
     ap.add_argument("--chain-ms", default="1,4", help="token counts of the chain; the first is `value`")
     ap.add_argument("--trials", type=int, default=11, help="per-cell timing trials")
     ap.add_argument("--replays", type=int, default=300, help="graph replays per per-cell trial")
@@ -530,11 +532,23 @@ MARKER = "zero_kernel"  # the library's K = 0 kernel: launched only as a separat
 TRACED_KERNELS = ("skg::", "read_tiles_kernel", "empty_kernel")
 
 
+def shape_key(text):
+    """'4096x1024' -> (4096, 1024); 'pair4096x128' -> ('pair', 4096, 128)."""
+    t = text.strip()
+    pair = t.startswith("pair")
+    n, k = (int(v) for v in t[4 if pair else 0:].split("x"))
+    return ("pair", n, k) if pair else (n, k)
+
+
 def traced_units(args):
     """Selection flags shared by the parent and the trace child."""
     if args.workload == "chain":
         cells = [] if args.no_cells else [(s, m) for s, m, _ in CELL_SHAPES]
         return cells, True
+    if args.workload == "cells":
+        ms = tuple(int(m) for m in args.ms.split(","))
+        shapes = [shape_key(t) for t in args.only.split(",")] if args.only else [s for s, _, _ in CELL_SHAPES]
+        return [(s, ms) for s in shapes], False
     return CELL_WORKLOADS[args.workload][1], False
 
 
@@ -653,7 +667,9 @@ def run_trace_child(args):
     os.makedirs(out_dir, exist_ok=True)
     cmd = [exe, "--kernel-trace", "--stats", "--output-format", "csv", "-d", out_dir, "-o", "trace",
            "--", sys.executable, os.path.abspath(__file__), "--trace-pass", "--workload", args.workload,
-           "--chain-ms", args.chain_ms]
+           "--chain-ms", args.chain_ms, "--ms", args.ms]
+    if args.only:
+        cmd += ["--only", args.only]
     for flag in ("no_cells", "no_dependent", "no_probe"):
         if getattr(args, flag):
             cmd.append("--" + flag.replace("_", "-"))
@@ -1077,7 +1093,9 @@ def main(argv=None) -> int:
                    "cores": nt, "kind": "oracle", "cpu_model": cpu_model(),
                    "sample": f"one call of each of the {len(cells)} cells, fp64 C oracle, median of 3 "
                              f"runs each, {s:.2f} s"}
-        config = {"workload": CELL_WORKLOADS[args.workload][0],
+        desc = (CELL_WORKLOADS[args.workload][0] if args.workload in CELL_WORKLOADS else
+                "cells " + ", ".join(cell_name(shape_cell(sh, m)) for sh, ms in cells_sel for m in ms))
+        config = {"workload": desc,
                   "launches_per_step": sum(u.launches for u in step_units), "bytes_per_step": step_bytes,
                   "rotation_bytes_min": ROTATE_BYTES, "accumulate": "fp32", "device": props.name,
                   "source_digest": source_digest()}

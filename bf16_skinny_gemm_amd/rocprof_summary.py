@@ -16,6 +16,12 @@ that ``--stats`` reports; ``--pmc`` counter CSVs (``FETCH_SIZE`` /
 duration, replay time per call, dependent chain, the read probe of the same
 size, CPU oracle, parity), the read probe per size and the empty-kernel floor.
 
+``--counter-table DIR [DIR ...]`` averages every counter of every ``--pmc`` pass
+given (one directory per pass, all over the same command) per (kernel, grid,
+workgroup) and prints the derived figures: loaded vector-memory latency, scalar
+(kernel-argument) load latency, mean waves per CU, translation-miss rate, L1→L2
+and L2→DRAM request latencies.
+
 ``--traffic`` writes the HBM-traffic record ``bench.py`` reads for its roofline:
 the average FETCH_SIZE and WRITE_SIZE per dispatch of one kernel (all of its
 dispatches, in the proportions the profiled command launched them), and the
@@ -139,6 +145,43 @@ def traffic_record(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kernel,
     return "\n".join(lines)
 
 
+def counter_table(dirs, filt="skg::"):
+    """Per (kernel, grid, workgroup): the mean of each counter over its dispatches,
+    pooled over the passes in `dirs`, and the figures derived from them."""
+    acc = {}
+    for d in dirs:
+        for p in _find(d, "counter_collection.csv"):
+            with open(p, newline="") as f:
+                for row in csv.DictReader(f):
+                    name = _col(row, "Kernel_Name") or ""
+                    if filt and filt not in name:
+                        continue
+                    key = (name, int(_col(row, "Grid_Size") or 0), int(_col(row, "Workgroup_Size") or 0))
+                    acc.setdefault(key, {}).setdefault(_col(row, "Counter_Name"), []).append(
+                        float(_col(row, "Counter_Value")))
+    out = []
+    for (name, grid, wg), c in sorted(acc.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        m = {k: statistics.mean(v) for k, v in c.items()}
+        g = lambda k: m.get(k, float("nan"))
+        miss, hit = g("TCP_UTCL1_TRANSLATION_MISS_sum"), g("TCP_UTCL1_TRANSLATION_HIT_sum")
+        out.append(f"{name.replace('void skg::', '').replace('(skg::Args)', '')}  blocks={grid // max(1, wg)} x {wg}")
+        out.append(f"    waves {g('SQ_WAVES'):.0f}, mean waves per CU {g('MeanOccupancyPerCU'):.1f}; "
+                   f"vector-memory latency {g('VmemLatency'):.0f} cycles, scalar-load latency "
+                   f"{g('SmemLatency'):.0f} cycles ({g('SQ_INSTS_SMEM') / max(1.0, g('SQ_WAVES')):.1f} per wave), "
+                   f"LDS latency {g('LdsLatency'):.0f} cycles, LDS bank-conflict cycles {g('SQ_LDS_BANK_CONFLICT'):.0f}")
+        out.append(f"    UTCL1 translations: {miss:.0f} misses / {hit:.0f} hits "
+                   f"({100 * miss / max(1.0, miss + hit):.2f}% miss); L1->L2 read latency "
+                   f"{g('TCP_TCC_READ_REQ_LATENCY_sum') / max(1.0, g('TCP_TCC_READ_REQ_sum')):.0f} cycles over "
+                   f"{g('TCP_TCC_READ_REQ_sum'):.0f} requests; L2->DRAM read latency "
+                   f"{g('TCC_EA0_RDREQ_LEVEL_sum') / max(1.0, g('TCC_EA0_RDREQ_sum')):.0f} cycles over "
+                   f"{g('TCC_EA0_RDREQ_sum'):.0f} requests; L2 hits {g('TCC_HIT_sum'):.0f}, misses {g('TCC_MISS_sum'):.0f}")
+        out.append(f"    instructions per wave: vmem reads {g('SQ_INSTS_VMEM_RD') / max(1.0, g('SQ_WAVES')):.1f}, "
+                   f"valu {g('SQ_INSTS_VALU') / max(1.0, g('SQ_WAVES')):.0f}, salu {g('SQ_INSTS_SALU') / max(1.0, g('SQ_WAVES')):.0f}; "
+                   f"TA busy {g('TA_TA_BUSY_sum'):.0f}, TD busy {g('TD_TD_BUSY_sum'):.0f}, "
+                   f"GRBM_GUI_ACTIVE {g('GRBM_GUI_ACTIVE'):.0f}")
+    return "\n".join(out)
+
+
 def _fmt(v, nd=3):
     return "n/a" if v is None else (f"{v:.{nd}f}" if isinstance(v, float) else str(v))
 
@@ -208,6 +251,7 @@ def main():
     ap.add_argument("--bench-json", help="render the tables of a bench.py JSON line")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--copy", nargs=2, metavar=("COPY_FETCH_DIR", "COPY_WRITE_DIR"))
+    ap.add_argument("--counter-table", nargs="+", metavar="DIR")
     ap.add_argument("--kernel", help="kernel name for --traffic")
     ap.add_argument("--digest", help="source digest for --traffic (bench.source_digest())")
     args = ap.parse_args()
@@ -215,6 +259,9 @@ def main():
         with open(args.bench_json) as f:
             line = [l for l in f if l.strip().startswith("{")][-1]
         print(bench_tables(json.loads(line)))
+        return 0
+    if args.counter_table:
+        print(counter_table(args.counter_table, args.filter or "skg::"))
         return 0
     if args.traffic:
         if not (args.copy and args.kernel and args.digest):
