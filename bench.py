@@ -474,7 +474,8 @@ def floor_group(ctx):
     units = []
     for nb in sorted(probe_sizes()):
         nviews = probe_copies(nb)
-        views = [torch.ones(nb, dtype=torch.uint8, device=ctx.dev) for _ in range(nviews)]
+        # random bytes, like the weights the cells stream (not a constant pattern)
+        views = [torch.randint(0, 256, (nb,), dtype=torch.uint8, device=ctx.dev) for _ in range(nviews)]
         for loads, threads in PROBE_SHAPES:
             words = probe.tiles_sink_words(nb, loads, threads)
             sink = torch.empty(words, dtype=torch.int32, device=ctx.dev)
