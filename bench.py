@@ -195,14 +195,6 @@ def copy_calibration() -> int:
     return 0
 
 
-def fit_line(xs, ys):
-    """Least-squares y = a + b x; returns (a, b)."""
-    n = len(xs)
-    mx, my = sum(xs) / n, sum(ys) / n
-    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
-    return my - b * mx, b
-
-
 def bytes_per_call(cell) -> int:
     """Algorithmic bytes of one call: the weight(s) once, x once, y once."""
     if cell[0] == "pair":
@@ -304,6 +296,7 @@ class Ctx:
 
         self.np, self.torch, self.skg = np, torch, skg
         self.args = args
+        self.capture_stream = None
         self.dev = torch.device("cuda:0")
         torch.cuda.set_device(self.dev)
         skg.skinny_gemm_init(0)
@@ -319,7 +312,9 @@ class Ctx:
     def capture(self, fn):
         torch = self.torch
         g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
+        if self.capture_stream is None:
+            self.capture_stream = torch.cuda.Stream()
+        s = self.capture_stream
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
             fn()  # eager warm-up on the capture stream
@@ -935,7 +930,7 @@ def attach_read_fractions(cells, reads):
             c["kernel_vs_read"] = round(r["best_kernel"]["kernel_us"] / c["kernel_us"], 4)
 
 
-def dominant_kernel(chain_row, cells):
+def dominant_kernel(chain_row):
     """The compiled kernel instance with the largest share of the headline step,
     the chain's shapes pooled by kernel name (as rocprofv3 --stats aggregates)."""
     pooled = {}
@@ -1057,7 +1052,7 @@ def main(argv=None) -> int:
         nt = oracle.default_threads()
     if with_chain:
         value, ms_per_step = headline["gbps"], headline["ms_per_step"]
-        roofline = dominant_kernel(headline, cells)
+        roofline = dominant_kernel(headline)
         cpu = None
         if want_cpu and "cpu_oracle_s_per_step" in headline:
             s = headline["cpu_oracle_s_per_step"]

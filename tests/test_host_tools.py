@@ -150,11 +150,6 @@ def test_refine_twins_add_the_lookahead_form(tmp_path):
     assert [(p.x_in_lds, p.grid_blocks) for p in plans] == [(1, 0), (2, 0), (1, 256), (2, 256)]
 
 
-def test_fit_line():
-    a, b = bench.fit_line([1.0, 2.0, 4.0], [3.0, 5.0, 9.0])
-    assert a == pytest.approx(1.0) and b == pytest.approx(2.0)
-
-
 def test_parse_grids_refine_tokens():
     assert sweep.parse_grids("same,balanced,tile") == (sweep.SAME, sweep.BALANCED, sweep.BIG_GRID)
 
@@ -299,3 +294,102 @@ def test_read_kernel_trace_orders_by_start(tmp_path):
     p.write_text("Kind,Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp\n"
                  "KERNEL_DISPATCH,2,b,200,300\nKERNEL_DISPATCH,1,a,100,150\n")
     assert bench.read_kernel_trace([str(p)]) == [(100, 150, "a"), (200, 300, "b")]
+
+
+def test_dominant_kernel_pools_shapes_by_kernel_name():
+    k1, k2 = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, 0, true, 1>(skg::Args)", "void skg::other(skg::Args)"
+    row = {"M": 1, "groups": [
+        {"shape": "(12576,4096)", "calls": 34, "kernel": k1, "bytes_per_call": 100_000_000, "event_us_per_call": 10.0,
+         "rocprof": {"avg_us": 11.0}},
+        {"shape": "(2048,4096)", "calls": 53, "kernel": k1, "bytes_per_call": 20_000_000, "event_us_per_call": 4.0,
+         "rocprof": {"avg_us": 4.5}},
+        {"shape": "(4096,4096)", "calls": 34, "kernel": k2, "bytes_per_call": 50, "event_us_per_call": 6.0}]}
+    r = bench.dominant_kernel(row)
+    assert r["kernel"] == k1 and r["launches_per_step"] == 87
+    assert r["avg_launch_us"] == pytest.approx((34 * 10 + 53 * 4) / 87, abs=1e-3)
+    bpl = (34 * 100_000_000 + 53 * 20_000_000) / 87
+    assert r["algorithmic_bytes_per_launch"] == round(bpl)
+    assert r["achieved"] == pytest.approx(bpl / (((34 * 10 + 53 * 4) / 87) * 1e-6) / 1e9, rel=1e-4)
+    assert r["rocprof_avg_launch_us"] == pytest.approx((34 * 11 + 53 * 4.5) / 87, abs=1e-3)
+    assert r["share_of_step"] == pytest.approx((34 * 10 + 53 * 4) / (34 * 10 + 53 * 4 + 34 * 6), abs=1e-4)
+
+
+def test_attach_read_fractions():
+    cells = [{"cell": "(4096,1024)M1", "weight_bytes": 8388608, "replay_us_per_call": 3.2, "kernel_us": 3.4},
+             {"cell": "(1,1)M1", "weight_bytes": 2, "replay_us_per_call": 1.0}]
+    reads = [{"bytes": 8388608, "best_replay": {"replay_us": 3.0}, "best_kernel": {"kernel_us": 3.1}}]
+    bench.attach_read_fractions(cells, reads)
+    assert cells[0]["replay_vs_read"] == pytest.approx(3.0 / 3.2, abs=1e-4)
+    assert cells[0]["kernel_vs_read"] == pytest.approx(3.1 / 3.4, abs=1e-4)
+    assert "replay_vs_read" not in cells[1]
+
+
+def _pmc_csv(path, rows):
+    path.parent.mkdir(parents=True, exist_ok=True)
+    head = "Dispatch_Id,Grid_Size,Workgroup_Size,Kernel_Name,Counter_Name,Counter_Value\n"
+    path.write_text(head + "".join(f"{i},{g},{w},\"{k}\",{c},{v}\n" for i, (g, w, k, c, v) in enumerate(rows)))
+
+
+def test_traffic_record_scales_by_the_copy(tmp_path):
+    from bf16_skinny_gemm_amd import rocprof_summary as rs
+
+    k = "void skg::fixed_k_kernel<1, 64, 4, 1, 2, 0, true, 1>(skg::Args)"
+    _pmc_csv(tmp_path / "f" / "a_counter_collection.csv",
+             [(1024, 256, k, "FETCH_SIZE", 100.0), (1024, 256, k, "FETCH_SIZE", 300.0),
+              (64, 64, "other", "FETCH_SIZE", 9999.0)])
+    _pmc_csv(tmp_path / "w" / "a_counter_collection.csv", [(1024, 256, k, "WRITE_SIZE", 2.0)])
+    _pmc_csv(tmp_path / "cf" / "a_counter_collection.csv", [(8, 8, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 131072.0)])
+    _pmc_csv(tmp_path / "cw" / "a_counter_collection.csv", [(8, 8, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 262144.0)])
+    rec = rs.traffic_record(str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                            k, "abc")
+    d = dict(line.split(": ", 1) for line in rec.splitlines())
+    assert float(d["fetch_kib_per_dispatch"]) == 200.0 and float(d["write_kib_per_dispatch"]) == 2.0
+    assert float(d["copy_fetch_factor"]) == 2.0 and float(d["copy_write_factor"]) == 1.0
+    assert int(d["hbm_bytes_per_dispatch"]) == 200 * 1024 * 2 + 2 * 1024
+    # and bench reads the record back when the digest and kernel match
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "traffic_chain.txt").write_text("# note\n" + rec + "\n")
+    import bench as b
+
+    old_root, old_digest = b.ROOT, b.source_digest
+    try:
+        b.ROOT, b.source_digest = str(tmp_path), (lambda: "abc")
+        assert b.recorded_traffic("chain", k) == 200 * 1024 * 2 + 2 * 1024
+    finally:
+        b.ROOT, b.source_digest = old_root, old_digest
+
+
+def test_counter_table_derives_rates(tmp_path):
+    from bf16_skinny_gemm_amd import rocprof_summary as rs
+
+    k = "void skg::fixed_k_kernel<4, 64, 8, 1, 1, 2, true, 2>(skg::Args)"
+    _pmc_csv(tmp_path / "p1" / "x_counter_collection.csv",
+             [(115200, 256, k, "SQ_WAVES", 1800.0), (115200, 256, k, "VmemLatency", 2342.0),
+              (115200, 256, k, "TCP_UTCL1_TRANSLATION_MISS_sum", 10.0),
+              (115200, 256, k, "TCP_UTCL1_TRANSLATION_HIT_sum", 990.0),
+              (115200, 256, k, "TCC_EA0_RDREQ_sum", 100.0), (115200, 256, k, "TCC_EA0_RDREQ_LEVEL_sum", 200000.0)])
+    out = rs.counter_table([str(tmp_path / "p1")])
+    assert "blocks=450 x 256" in out and "waves 1800" in out
+    assert "vector-memory latency 2342 cycles" in out and "(1.00% miss)" in out
+    assert "L2->DRAM read latency 2000 cycles" in out
+
+
+def test_bench_tables_render_a_line():
+    from bf16_skinny_gemm_amd import rocprof_summary as rs
+
+    line = {"chains": [{"M": 1, "ms_per_step": 1.4, "calls": 186, "gbps": 5400.0, "frac_of_peak": 0.675,
+                        "parity": {"pass": True, "outputs_checked": 186, "elements": 10, "max_g1_ratio": 0.1,
+                                   "max_s1_ratio": 0.9, "min_row_cosine": 0.99999999},
+                        "groups": [{"shape": "(4096,4096)", "calls": 34, "kernel": "void skg::k(skg::Args)",
+                                    "event_us_per_call": 6.7, "event_frac": 0.626}]}],
+            "cells": [{"cell": "(4096,4096)M1", "replay_us_per_call": 6.69, "replay_frac": 0.627,
+                       "read_probe_replay_us": 6.55, "rocprof": {"avg_us": 7.0, "med_us": 6.9}, "kernel_frac": 0.6,
+                       "cpu_oracle_us": 2876.0, "parity": {"pass": True}}],
+            "read_probe": [{"bytes": 8, "best_replay": {"loads": 4, "threads": 256, "replay_us": 1.0},
+                            "replay_gbps": 0.01, "all": [{"loads": 4, "threads": 256, "replay_us": 1.0}]}],
+            "empty_kernel": [{"grid": 1, "replay_us_per_launch": 1.56}]}
+    out = rs.bench_tables(line)
+    assert "1400.0 µs per step of 186 calls" in out and "| (4096,4096) | 34 | `k(skg::Args)` | 6.700 | 62.6 |" in out
+    assert "| (4096,4096)M1 | 7.000 (6.900) | 60.0 | 6.690 | 62.7 |" in out
+    assert "| 1 | 1.56 | n/a |" in out
