@@ -209,9 +209,11 @@ def bench_tables(d):
     if d.get("cells"):
         out.append("### Cells (cold cache, >= 1 GiB of rotated copies)")
         out.append("")
+        vendor = any("vendor_us_per_call" in c for c in d["cells"])
         out.append("| cell | rocprof avg µs (med) | % of 8 TB/s | replay µs/call | % | dependent µs/call | "
-                   "read probe µs (replay) | replay ÷ probe | CPU oracle µs | parity |")
-        out.append("|---|---|---|---|---|---|---|---|---|---|")
+                   "read probe µs (replay) | replay ÷ probe | CPU oracle µs | parity |"
+                   + (" F.linear µs/call | F.linear ÷ skinny |" if vendor else ""))
+        out.append("|---|---|---|---|---|---|---|---|---|---|" + ("---|---|" if vendor else ""))
         for c in d["cells"]:
             rp = c.get("rocprof", {})
             kern = f"{_fmt(rp.get('avg_us'))} ({_fmt(rp.get('med_us'))})" if rp else "n/a"
@@ -220,7 +222,9 @@ def bench_tables(d):
                        f"{c['replay_us_per_call']:.3f} | {100 * c['replay_frac']:.1f} | "
                        f"{_fmt(c.get('dependent_us_per_call'))} | {_fmt(c.get('read_probe_replay_us'))} | "
                        f"{_fmt(ratio)} | {_fmt(c.get('cpu_oracle_us'), 1)} | "
-                       f"{c.get('parity', {}).get('pass', 'n/a')} |")
+                       f"{c.get('parity', {}).get('pass', 'n/a')} |"
+                       + (f" {_fmt(c.get('vendor_us_per_call'))} | {_fmt(c.get('speedup_vs_vendor'))} |"
+                          if vendor else ""))
         out.append("")
     if d.get("read_probe"):
         out.append("### Read-only probe (one block per tile, each size over >= 1 GiB of buffers)")
