@@ -380,6 +380,51 @@ def test_graph_replay_bitwise(skg):
         del g
 
 
+def test_graph_dependent_chain_runs_in_order(skg):
+    """Calls captured into one graph on one stream run in stream order: a chain whose
+    call i+1 reads the first M*K outputs of call i (every output set to NaN before
+    each replay, so a call that ran early would read NaN) replays bit for bit like the
+    same calls run one at a time with the device synchronised after each. The decode
+    benchmark times its calls on this ordering."""
+    N, K = 4096, 1024
+    for M in (1, 4):
+        Ws = [to_dev(synth.weights(N, K, seed=40, tensor_id=i)) for i in range(6)]
+        x0 = to_dev(synth.activations(M, K, seed=41))
+        outs = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in Ws]
+        xs = [x0] + [o.view(-1)[:M * K].view(M, K) for o in outs[:-1]]
+
+        def chain():
+            for x, W, y in zip(xs, Ws, outs):
+                skg.gemm(x, W, out=y)
+
+        ref = []
+        for x, W in zip(xs, Ws):
+            y = skg.gemm(x, W)
+            torch.cuda.synchronize()
+            ref.append(y)
+            if len(ref) < len(Ws):
+                # the next eager call reads this output through xs
+                outs[len(ref) - 1].copy_(y)
+                torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            chain()
+            with torch.cuda.graph(g, stream=s):
+                chain()
+        torch.cuda.current_stream().wait_stream(s)
+        for rep in range(3):
+            for o in outs:
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for i, (o, r) in enumerate(zip(outs, ref)):
+                assert torch.equal(o.view(torch.int16), r.view(torch.int16)), (M, rep, i)
+        del g
+
+
 def test_concurrent_host_threads(skg):
     """Entry points called from several host threads at once, each on its own stream,
     through plans and M values whose lazily filled host caches (occupancy, static LDS,
