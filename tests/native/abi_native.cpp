@@ -214,7 +214,9 @@ int main()
         HIP_OK(hipMemsetAsync(y0d, 0, y0.size() * 2, stream));
         HIP_OK(hipStreamSynchronize(stream));
         HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
-        CHECK(skinny_gemm_bf16_pair(xmd, W0d, W1d, y0d, y1d, M, N, K, stream) == SKINNY_OK, "capture");
+        // the same call that produced e0: x rows at stride ldx
+        CHECK(skinny_gemm_bf16_pair_strided(xmd, xmd, ldx, W0d, W1d, y0d, y1d, N, M, N, K, stream) == SKINNY_OK,
+              "capture");
         HIP_OK(hipStreamEndCapture(stream, &graph));
         HIP_OK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
         for (int rep = 0; rep < 3; ++rep) {
