@@ -126,7 +126,7 @@ def parse(argv=None):
                     help="also time torch.nn.functional.linear on every cell (informational)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 256 MiB (PMC counter calibration)")
-    ap.add_argument("--read-ceiling", action="store_true",
+    ap.add_argument("--read-probe", action="store_true",
                     help="only run the read probe at every weight size and the empty-kernel floor")
     return ap.parse_args(argv)
 
@@ -996,13 +996,13 @@ def main(argv=None) -> int:
         return trace_pass(args)
     if args.copy_calibration:
         return copy_calibration()
-    if args.read_ceiling:
+    if args.read_probe:
         args.no_cells, args.workload = True, "chain"
 
     # the kernel-trace child runs first, before this process touches the GPU
     trace, trace_note = None, "skipped (--no-trace)"
-    if args.read_ceiling:
-        trace_note = "skipped (--read-ceiling)"
+    if args.read_probe:
+        trace_note = "skipped (--read-probe)"
     elif not args.no_trace:
         if under_profiler():
             trace_note = "skipped: this process already runs under a profiler"
@@ -1019,7 +1019,7 @@ def main(argv=None) -> int:
     log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
     want_parity, want_cpu = not args.no_parity, not args.no_cpu
 
-    if args.read_ceiling:
+    if args.read_probe:
         units, _ = floor_group(ctx)
         reads, empties = time_floor_units(ctx, units, args, None)
         print(json.dumps({"read_probe": reads, "empty_kernel": empties}), flush=True)

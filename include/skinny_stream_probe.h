@@ -1,6 +1,8 @@
 /* Read-stream probe: the rate at which a plain streaming kernel reads HBM on this
- * device, the practical ceiling beside which the GEMV's weight stream is judged
- * (the 8 TB/s peak is a datasheet figure). Measurement only; not part of the GEMM.
+ * device, a measured reference beside which the GEMV's weight stream is judged
+ * (the 8 TB/s peak is a datasheet figure). It is not an upper bound: a GEMV plan
+ * tuned per shape can read as fast or faster. Measurement only; not part of the
+ * GEMM.
  *
  * The measured-ceiling comparison follows vLLM PR #65306 (SM90 skinny GEMM plans),
  * section Validation, which rates the kernels by weight bytes per second against
