@@ -13,9 +13,13 @@ Python ints; a non-zero status raises :class:`SkinnyError`):
     skinny_gemm_bf16_pair_strided_ex, skinny_gemm_bf16_f32out,
     skinny_gemm_bf16_f32out_ex, skinny_gemm_get_plan,
     skinny_gemm_num_variants, skinny_gemm_get_variant,
-    skinny_gemm_status_string, skinny_gemm_version
+    skinny_gemm_status_string, skinny_gemm_version,
+    skinny_gemm_split_k_workspace_bytes, skinny_gemm_bf16_split_k,
+    skinny_gemm_split_k_num_variants,
+    skinny_gemm_split_k_get_variant, skinny_gemm_split_k_default_plan
 
-Tensor helpers: :func:`gemm`, :func:`gemm_pair` and :func:`gemm_pair_strided`.
+Tensor helpers: :func:`gemm`, :func:`gemm_pair`, :func:`gemm_pair_strided`,
+:func:`split_k_workspace` and :func:`gemm_split_k`.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ SKINNY_KIND_FIXED_K = 1
 SKINNY_KIND_LOOP_K = 2
 SKINNY_KIND_SCALAR = 3
 SKINNY_KIND_MFMA = 4
+SKINNY_KIND_SPLIT_K = 5
 
 
 class SkinnyError(RuntimeError):
@@ -106,11 +111,20 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_status_string.argtypes = [i]
         L.skinny_gemm_status_string.restype = ctypes.c_char_p
         L.skinny_gemm_version.argtypes = []
+        L.skinny_gemm_split_k_workspace_bytes.argtypes = [i, i, i, pp]
+        L.skinny_gemm_split_k_workspace_bytes.restype = ctypes.c_size_t
+        L.skinny_gemm_bf16_split_k.argtypes = [vp, vp, vp, i, i, i, pp, vp, ctypes.c_size_t, vp]
+        L.skinny_gemm_split_k_num_variants.argtypes = []
+        L.skinny_gemm_split_k_get_variant.argtypes = [i, pp]
+        L.skinny_gemm_split_k_default_plan.argtypes = [i, i, i, pp]
         for name in ("skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair",
                      "skinny_gemm_bf16_ex", "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out",
                      "skinny_gemm_bf16_f32out_ex", "skinny_gemm_bf16_pair_strided",
                      "skinny_gemm_bf16_pair_strided_ex", "skinny_gemm_get_plan",
-                     "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version"):
+                     "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version",
+                     "skinny_gemm_bf16_split_k",
+                     "skinny_gemm_split_k_num_variants", "skinny_gemm_split_k_get_variant",
+                     "skinny_gemm_split_k_default_plan"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
         return L
@@ -207,6 +221,43 @@ def skinny_gemm_version() -> int:
 
 def variants() -> list[Plan]:
     return [skinny_gemm_get_variant(i) for i in range(skinny_gemm_num_variants())]
+
+
+def _plan_ref(plan: Plan | None):
+    return ctypes.byref(plan) if plan is not None else None
+
+
+def skinny_gemm_split_k_workspace_bytes(M: int, N: int, K: int, plan: Plan | None = None) -> int:
+    """Workspace bytes of a split-K call (0: no call with these arguments is accepted)."""
+    return int(lib().skinny_gemm_split_k_workspace_bytes(M, N, K, _plan_ref(plan)))
+
+
+def skinny_gemm_bf16_split_k(x: int, W: int, y: int, M: int, N: int, K: int, plan: Plan | None,
+                             workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_split_k(x, W, y, M, N, K, _plan_ref(plan), workspace,
+                                          workspace_bytes, stream), "skinny_gemm_bf16_split_k")
+
+
+def skinny_gemm_split_k_num_variants() -> int:
+    return lib().skinny_gemm_split_k_num_variants()
+
+
+def skinny_gemm_split_k_get_variant(index: int) -> Plan:
+    p = Plan()
+    _check(lib().skinny_gemm_split_k_get_variant(index, ctypes.byref(p)),
+           "skinny_gemm_split_k_get_variant")
+    return p
+
+
+def skinny_gemm_split_k_default_plan(M: int, N: int, K: int) -> Plan:
+    p = Plan()
+    _check(lib().skinny_gemm_split_k_default_plan(M, N, K, ctypes.byref(p)),
+           "skinny_gemm_split_k_default_plan")
+    return p
+
+
+def split_k_variants() -> list[Plan]:
+    return [skinny_gemm_split_k_get_variant(i) for i in range(skinny_gemm_split_k_num_variants())]
 
 
 # ---- tensor helpers ---------------------------------------------------------
@@ -383,8 +434,54 @@ def gemm_pair_strided(x0: torch.Tensor, x1: torch.Tensor, W0: torch.Tensor, W1: 
     return out0, out1
 
 
+def split_k_workspace(M: int, N: int, K: int, plan: Plan | None = None,
+                      device: torch.device | str = "cuda") -> torch.Tensor:
+    """A zero-filled uint8 device buffer big enough for split-K calls of this shape
+    and plan (allocate it once, outside any graph capture, and reuse it)."""
+    nbytes = skinny_gemm_split_k_workspace_bytes(M, N, K, plan)
+    if nbytes == 0:
+        raise SkinnyError(SKINNY_ERR_INVALID_ARG, "skinny_gemm_split_k_workspace_bytes")
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def _split_args(x: torch.Tensor, W: torch.Tensor, out: torch.Tensor | None):
+    _check_tensor(x, "x")
+    _check_tensor(W, "W")
+    M, K = x.shape
+    N, K2 = W.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: x {tuple(x.shape)}, W {tuple(W.shape)}")
+    if W.device != x.device:
+        raise ValueError("x and W must be on the same device")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if out.device != x.device or tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be a contiguous bfloat16 [{M}, {N}] tensor on {x.device}")
+    return M, N, K, out
+
+
+def gemm_split_k(x: torch.Tensor, W: torch.Tensor, workspace: torch.Tensor,
+                 plan: Plan | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ W.T with cross-block split-K (skinny_gemm_bf16_split_k), partials in
+    `workspace` (from split_k_workspace, reused across calls on one stream)."""
+    M, N, K, out = _split_args(x, W, out)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {x.device}")
+    s = _stream_handle(x.device)
+    with _on_device(x.device):
+        skinny_gemm_bf16_split_k(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, plan,
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(), s)
+    return out
+
+
 __all__ = [
     "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair", "gemm_pair_strided",
+    "split_k_variants", "split_k_workspace", "gemm_split_k",
+    "skinny_gemm_split_k_workspace_bytes", "skinny_gemm_bf16_split_k",
+    "skinny_gemm_split_k_num_variants",
+    "skinny_gemm_split_k_get_variant", "skinny_gemm_split_k_default_plan", "SKINNY_KIND_SPLIT_K",
     "skinny_gemm_bf16_pair_strided", "skinny_gemm_bf16_pair_strided_ex",
     "skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",
     "skinny_gemm_bf16_pair_ex", "skinny_gemm_bf16_f32out", "skinny_gemm_bf16_f32out_ex",

@@ -26,7 +26,7 @@ LIB_NAME = "libskinny_gemm_bf16.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = "gfx950"
 SOURCES = ("skinny_gemm.hip", "variants_fixed_small.hip", "variants_fixed_k4096.hip",
-           "variants_fixed_k8192.hip", "variants_other.hip")
+           "variants_fixed_k8192.hip", "variants_other.hip", "split_k.hip")
 PROBE_LIB_PATH = os.path.join(HERE, "libskinny_stream_probe.so")
 PROBE_SOURCES = ("stream_probe.hip",)
 

@@ -1,0 +1,412 @@
+// Cross-block split-K (include/skinny_gemm.h, skinny_gemm_bf16_split_k): the K
+// range of every row is cut into S slices taken by S different blocks, whose
+// float32 partial sums meet in a global workspace; the last block of a tile to
+// arrive adds them in slice order and writes the output. One launch, no second
+// reduce kernel: the single-launch form of the split-K + reduce kernel pair that
+// vLLM PR #65306 (SM90 skinny GEMM plans), section Details, counts against
+// cuBLAS on its small-N / large-K shapes.
+//
+// Per slice the arithmetic is that of the compile-time-K kernel (kernels.hpp,
+// fixed_k_kernel) with k_split = S: lane (sub, kl) of a wave reads, for row
+// r * 64/LPR + sub and chunk j < CH, the 8 elements at s*KS + j*LPR*8 + kl*8 with
+// KS = LPR*8*CH; products go through v_dot2c_f32_bf16 in chunk order, the lanes
+// of a row meet by the same DPP butterfly, and the S slice sums are added as
+// ((p0 + p1) + p2) + ... So a split-K plan gives the same bits as the in-block
+// plan with the same (lanes_per_row, chunks, k_split = S).
+//
+// Hand-off between blocks, with no block ever waiting for another:
+//   1. every lane that holds a row sum stores it to part[s][m][row];
+//   2. each thread fences (release, agent scope: its stores reach the device
+//      coherence point, past the per-XCD L2), then the block meets at a barrier;
+//   3. one thread adds 1 to the tile's arrival counter (acq_rel, agent scope);
+//      the block that sees S - 1 there is the last of its tile;
+//   4. the last block fences (acquire, agent scope), adds the S partials of each
+//      of its outputs in slice order, rounds once to bfloat16, stores y, and
+//      sets the counter back to 0.
+// Counters therefore hold 0 between calls; partials are always written before
+// they are read, so they need no clearing.
+#include "skinny_gemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <mutex>
+
+#include "kernels.hpp"
+#include "validate.hpp"
+
+namespace skg {
+
+struct SplitArgs {
+    const uint16_t *x;   // [M][K], contiguous
+    const uint16_t *w;   // [N][K]
+    uint16_t *y;         // [M][N] bfloat16
+    float *part;         // [S][M][N] float32 partial sums
+    unsigned *count;     // [tiles] arrival counters, 0 between calls
+    int N, K, splits, tiles;
+};
+
+template <int M, int LPR, int CH, int R, bool NT>
+__global__ __launch_bounds__(kMaxWaves * 64) void split_k_kernel(SplitArgs a)
+{
+    constexpr int KS = LPR * 8 * CH;
+    constexpr int RPI = 64 / LPR;
+    constexpr int ROWS_W = R * RPI;
+    constexpr int OUT = sum_lane<LPR>();
+    const int rows_t = (int)(blockDim.x >> 6) * ROWS_W;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sub = lane / LPR;
+    const int kl = lane % LPR;
+    // the S blocks of a tile are consecutive, so they run and finish together
+    const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.splits);
+    const int s = __builtin_amdgcn_readfirstlane((int)blockIdx.x - tile * a.splits);
+    const int K = a.K;
+    const unsigned kbase = (unsigned)(s * KS + kl * 8);
+
+    // this wave's rows: a resource ending at the last valid one (rows >= N read 0)
+    const int row0 = tile * rows_t + wave * ROWS_W;
+    int valid = a.N - row0;
+    valid = valid < 0 ? 0 : (valid > ROWS_W ? ROWS_W : valid);
+    const __amdgpu_buffer_rsrc_t ws =
+        make_rsrc(valid > 0 ? a.w + (size_t)row0 * K : a.w, (unsigned)(valid * K * 2));
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(a.x, (unsigned)(M * K * 2));
+
+    u32x4 wv[R][CH], xr[M][CH];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            wv[r][j] = load16<NT>(ws, ((unsigned)((r * RPI + sub) * K) + kbase + j * LPR * 8) * 2u);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+            xr[m][j] = load16<false>(xs, ((unsigned)(m * K) + kbase + j * LPR * 8) * 2u);
+
+    float acc[M][R];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[m][r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                acc[m][r] = dot8(wv[r][j], xr[m][j], acc[m][r]);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            acc[m][r] = group_sum<LPR>(acc[m][r]);
+
+    // 1. partial sums of this slice
+    const size_t plane = (size_t)M * a.N;
+    if (kl == OUT) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = row0 + r * RPI + sub;
+            if (row < a.N) {
+#pragma unroll
+                for (int m = 0; m < M; ++m)
+                    a.part[(size_t)s * plane + (size_t)m * a.N + row] = acc[m][r];
+            }
+        }
+    }
+    // 2.-3. publish them and count this block in
+    __shared__ int last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned before =
+            __hip_atomic_fetch_add(&a.count[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == (unsigned)(a.splits - 1);
+    }
+    __syncthreads();
+    if (!last)
+        return;  // block-uniform
+
+    // 4. the last block of the tile: every other slice's partials are visible now
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int base = tile * rows_t;
+    for (int i = (int)threadIdx.x; i < M * rows_t; i += (int)blockDim.x) {
+        const int m = i / rows_t;
+        const int row = base + (i - m * rows_t);
+        if (row < a.N) {
+            const size_t o = (size_t)m * a.N + row;
+            float v = a.part[o];
+            for (int q = 1; q < a.splits; ++q)
+                v += a.part[(size_t)q * plane + o];
+            a.y[o] = f32_to_bf16(v);
+        }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&a.count[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace skg
+
+namespace {
+
+using namespace skg_host;
+
+// --- compiled split-K variants ---------------------------------------------
+
+struct SplitVariant {
+    skinny_plan_t plan;       // k_split = 0 in the table: S is chosen per call
+    const void *fn[kMaxM];    // NULL where x and the weights would not fit the register budget
+    int slice_k;              // KS = lanes_per_row * 8 * chunks
+    int rows_per_group;       // rows one wave covers
+};
+
+// Registers per lane: x takes 4*M*CH VGPRs, the weights 4*R*CH, the sums M*R;
+// the same budget as the compile-time-K family with x in registers.
+constexpr bool split_fits(int M, int CH, int R) { return M * CH <= 32 && 4 * (M * CH + R * CH) + M * R <= 200; }
+
+template <int M, int LPR, int CH, int R>
+constexpr const void *split_fn()
+{
+    if constexpr (split_fits(M, CH, R))
+        return reinterpret_cast<const void *>(&skg::split_k_kernel<M, LPR, CH, R, true>);
+    else
+        return nullptr;
+}
+
+template <int LPR, int CH, int R>
+SplitVariant split_variant()
+{
+    SplitVariant v{};
+    v.plan = skinny_plan_t{SKINNY_KIND_SPLIT_K, 256, LPR, CH, R, 0, 1, 0, 0, 0};
+    v.fn[0] = split_fn<1, LPR, CH, R>();
+    v.fn[1] = split_fn<2, LPR, CH, R>();
+    v.fn[2] = split_fn<3, LPR, CH, R>();
+    v.fn[3] = split_fn<4, LPR, CH, R>();
+    v.fn[4] = split_fn<5, LPR, CH, R>();
+    v.fn[5] = split_fn<6, LPR, CH, R>();
+    v.fn[6] = split_fn<7, LPR, CH, R>();
+    v.fn[7] = split_fn<8, LPR, CH, R>();
+    v.slice_k = LPR * 8 * CH;
+    v.rows_per_group = R * (64 / LPR);
+    return v;
+}
+
+// Slices of 512..4096 elements at 64 lanes per row (K = 1024..32768 over 2..8
+// slices), and of 256 / 512 / 768 at 32 lanes per row (K = 1536 in two).
+const SplitVariant kSplit[] = {
+    split_variant<64, 1, 1>(), split_variant<64, 2, 1>(), split_variant<64, 4, 1>(), split_variant<64, 8, 1>(),
+    split_variant<64, 1, 2>(), split_variant<64, 2, 2>(), split_variant<64, 4, 2>(),
+    split_variant<32, 1, 1>(), split_variant<32, 2, 1>(), split_variant<32, 3, 1>(),
+};
+constexpr int kNumSplit = sizeof(kSplit) / sizeof(kSplit[0]);
+
+const SplitVariant *find_split(const skinny_plan_t &p)
+{
+    for (const SplitVariant &v : kSplit)
+        if (v.plan.lanes_per_row == p.lanes_per_row && v.plan.chunks == p.chunks &&
+            v.plan.rows_per_wave == p.rows_per_wave)
+            return &v;
+    return nullptr;
+}
+
+// Default split-K plan for K: 256 threads, one row per wave at 64 lanes per row,
+// the most slices in {4, 2, 8} order whose slice a compiled variant covers
+// (K = 4096: 4 slices of 1024); else 32 lanes per row.
+bool default_split(int K, int M, skinny_plan_t *out)
+{
+    const int order[] = {4, 2, 8};
+    for (int lpr : {64, 32}) {
+        for (int S : order) {
+            if (K % S != 0)
+                continue;
+            for (const SplitVariant &v : kSplit) {
+                if (v.plan.lanes_per_row == lpr && v.plan.rows_per_wave == 1 && v.slice_k * S == K &&
+                    v.fn[M - 1]) {
+                    *out = v.plan;
+                    out->k_split = S;
+                    return true;
+                }
+            }
+        }
+    }
+    return false;
+}
+
+int split_plan_ok(const skinny_plan_t &p, const SplitVariant *v, int K, int M)
+{
+    if (p.kind != SKINNY_KIND_SPLIT_K)
+        return SKINNY_ERR_INVALID_ARG;
+    if (!v)
+        return SKINNY_ERR_UNSUPPORTED;
+    const int tpb = p.threads_per_block;
+    if (tpb < 64 || tpb > skg::kMaxWaves * 64 || tpb % 64 != 0)
+        return SKINNY_ERR_INVALID_ARG;
+    if (p.k_split < 1 || p.k_split > 64 || p.nontemporal != 1 || p.grid_blocks != 0 || p.x_in_lds != 0 ||
+        p.prefetch != 0)
+        return SKINNY_ERR_INVALID_ARG;
+    if (K != v->slice_k * p.k_split)
+        return SKINNY_ERR_INVALID_ARG;
+    if (!v->fn[M - 1])
+        return SKINNY_ERR_UNSUPPORTED;
+    return SKINNY_OK;
+}
+
+// Workspace layout, the same for every call: kCountWords 32-bit arrival counters
+// (tile t uses word t) in the first 64 KiB, then the float partials [S][M][N].
+// Counters stay at zero between calls and no call writes partials over them, so
+// one workspace serves calls of any shape it is large enough for.
+constexpr size_t kCountWords = 16384;
+constexpr size_t kPartOffset = kCountWords * 4;
+
+struct SplitLayout {
+    size_t part_bytes, total;
+    int tiles;
+};
+
+SplitLayout split_layout(const skinny_plan_t &p, const SplitVariant *v, int M, int N)
+{
+    SplitLayout l{};
+    const int rows_t = (p.threads_per_block / 64) * v->rows_per_group;
+    l.tiles = (int)(((long long)N + rows_t - 1) / rows_t);
+    l.part_bytes = (size_t)p.k_split * (size_t)M * (size_t)N * 4;
+    l.total = kPartOffset + l.part_bytes;
+    return l;
+}
+
+// A resolved split-K call: plan, variant and layout, all checked.
+struct SplitCall {
+    skinny_plan_t plan;
+    const SplitVariant *v;
+    SplitLayout lay;
+};
+
+// Checks of a split-K call that need no device: the common argument checks, the
+// vector-path conditions and the plan. *empty is set for calls with nothing to do.
+int split_prepare(const Call &c, const skinny_plan_t *plan_in, SplitCall *out, bool *empty)
+{
+    *empty = false;
+    int st = validate(c);
+    if (st != SKINNY_OK)
+        return st;
+    if (c.M == 0 || c.N == 0) {
+        *empty = true;
+        return SKINNY_OK;
+    }
+    if (c.K == 0 || !vector_ok(c) || !out_span_ok(c))
+        return SKINNY_ERR_INVALID_ARG;
+    skinny_plan_t p;
+    if (plan_in) {
+        p = *plan_in;
+    } else if (!default_split(c.K, c.M, &p)) {
+        return SKINNY_ERR_UNSUPPORTED;
+    }
+    const SplitVariant *v = find_split(p);
+    st = split_plan_ok(p, v, c.K, c.M);
+    if (st != SKINNY_OK)
+        return st;
+    // each wave's buffer resource spans its rows; partial and output indices fit
+    if ((long long)v->rows_per_group * c.K * 2 > 0x7FFFFFFFLL)
+        return SKINNY_ERR_INVALID_ARG;
+    out->plan = p;
+    out->v = v;
+    out->lay = split_layout(p, v, c.M, c.N);
+    if ((size_t)out->lay.tiles > kCountWords)
+        return SKINNY_ERR_INVALID_ARG;
+    return SKINNY_OK;
+}
+
+hipError_t split_launch(const Call &c, const SplitCall &sc, void *workspace, hipStream_t stream)
+{
+    skg::SplitArgs a{};
+    a.x = static_cast<const uint16_t *>(c.x);
+    a.w = static_cast<const uint16_t *>(c.w0);
+    a.y = static_cast<uint16_t *>(c.y0);
+    a.count = static_cast<unsigned *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kPartOffset);
+    a.N = c.N;
+    a.K = c.K;
+    a.splits = sc.plan.k_split;
+    a.tiles = sc.lay.tiles;
+    void *args[] = {&a};
+    const long long grid = (long long)sc.lay.tiles * sc.plan.k_split;
+    const hipError_t e = hipLaunchKernel(sc.v->fn[c.M - 1], dim3((unsigned)grid),
+                                         dim3((unsigned)sc.plan.threads_per_block), args, 0, stream);
+    if (e != hipSuccess)
+        (void)hipGetLastError();
+    return e;
+}
+
+int check_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SKINNY_ERR_UNSUPPORTED;
+    }
+    return skinny_gemm_init(dev);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t skinny_gemm_split_k_workspace_bytes(int M, int N, int K, const skinny_plan_t *plan)
+{
+    if (M < 1 || M > kMaxM || N < 1 || K < 1)
+        return 0;
+    skinny_plan_t p;
+    if (plan) {
+        p = *plan;
+    } else if (!default_split(K, M, &p)) {
+        return 0;
+    }
+    const SplitVariant *v = find_split(p);
+    if (split_plan_ok(p, v, K, M) != SKINNY_OK)
+        return 0;
+    const SplitLayout l = split_layout(p, v, M, N);
+    return (size_t)l.tiles > kCountWords ? 0 : l.total;
+}
+
+int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N, int K,
+                             const skinny_plan_t *plan, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    const Call c = single_call(x, W, y, M, N, K, 0);
+    SplitCall sc;
+    bool empty = false;
+    int st = split_prepare(c, plan, &sc, &empty);
+    if (st != SKINNY_OK || empty)
+        return st;
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < sc.lay.total)
+        return SKINNY_ERR_INVALID_ARG;
+    const size_t xb = span(M, K, K, 2), wb = (size_t)N * K * 2, yb = (size_t)M * N * 2;
+    if (overlaps(workspace, sc.lay.total, x, xb) || overlaps(workspace, sc.lay.total, W, wb) ||
+        overlaps(workspace, sc.lay.total, y, yb))
+        return SKINNY_ERR_INVALID_ARG;
+    st = check_current_device();
+    if (st != SKINNY_OK)
+        return st;
+    return split_launch(c, sc, workspace, stream) == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
+}
+
+int skinny_gemm_split_k_num_variants(void) { return kNumSplit; }
+
+int skinny_gemm_split_k_get_variant(int index, skinny_plan_t *out)
+{
+    if (index < 0 || index >= kNumSplit || !out)
+        return SKINNY_ERR_INVALID_ARG;
+    *out = kSplit[index].plan;
+    return SKINNY_OK;
+}
+
+int skinny_gemm_split_k_default_plan(int M, int N, int K, skinny_plan_t *out)
+{
+    if (!out || M < 1 || M > kMaxM || N < 1 || K < 1)
+        return SKINNY_ERR_INVALID_ARG;
+    return default_split(K, M, out) ? SKINNY_OK : SKINNY_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -54,6 +54,7 @@
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -77,9 +78,12 @@ typedef enum skinny_kind {
                                 x in registers or LDS, tiles optionally software-pipelined */
     SKINNY_KIND_LOOP_K = 2,  /* any K % 8 == 0; x staged in LDS; chunks = loads in flight per row */
     SKINNY_KIND_SCALAR = 3,  /* any K, any alignment; element-wise loads */
-    SKINNY_KIND_MFMA = 4     /* K % (128*k_split*chunks) == 0; 4-row groups on the matrix
+    SKINNY_KIND_MFMA = 4,    /* K % (128*k_split*chunks) == 0; 4-row groups on the matrix
                                 cores (v_mfma_f32_4x4x4_16b_bf16), x staged in LDS,
                                 chunks = loads per group per K batch, lanes_per_row = 16 */
+    SKINNY_KIND_SPLIT_K = 5  /* cross-block split-K, only through skinny_gemm_bf16_split_k*:
+                                K = k_split*lanes_per_row*8*chunks, k_split blocks per row
+                                tile each take one K slice, partials in a workspace */
 } skinny_kind_t;
 
 /* One launch configuration ("plan"): the knobs of the plan tuple of vLLM PR
@@ -195,6 +199,54 @@ int skinny_gemm_get_plan(int N, int K, int M, skinny_plan_t *out);
  * SKINNY_ERR_INVALID_ARG for an index out of range. Host-only. */
 int skinny_gemm_num_variants(void);
 int skinny_gemm_get_variant(int index, skinny_plan_t *out);
+
+/* ---- Cross-block split-K ------------------------------------------------------
+ * y = x . W^T in ONE launch where the K range of every row is cut into S slices
+ * (plan.k_split) that S different blocks take: the single-launch form of the
+ * split-K + reduce kernel pair that vLLM PR #65306 (SM90 skinny GEMM plans),
+ * section Details, counts against cuBLAS on its small-N / large-K shapes. Each
+ * block stores its float32 partial sums in a workspace, and the last block of a
+ * row tile to arrive (a per-tile arrival counter, agent-scope release/acquire)
+ * adds the S partials in slice order 0..S-1 and writes bfloat16 y. No block waits
+ * for another. The result equals, bit for bit, that of the FIXED_K plan with the
+ * same (lanes_per_row, chunks) and k_split = S.
+ *
+ * Plans: kind SKINNY_KIND_SPLIT_K, a variant from skinny_gemm_split_k_get_variant
+ * with k_split = S >= 1 set by the caller, threads_per_block a multiple of 64 in
+ * 64..512, nontemporal 1, grid_blocks 0 (one block per row tile and slice),
+ * x_in_lds 0, prefetch 0; K must equal S * lanes_per_row * 8 * chunks. plan ==
+ * NULL picks a default (256 threads, one row per wave, S in 4, 2, 8 order) or
+ * returns SKINNY_ERR_UNSUPPORTED when no compiled slice fits K.
+ *
+ * Same conventions as skinny_gemm_bf16 for x, W, y, M, N, K and stream, except:
+ * x and W must be 16-byte aligned and K % 8 == 0 (there is no element-wise
+ * path: SKINNY_ERR_INVALID_ARG otherwise), K > 0, and only bfloat16 output. */
+
+/* Bytes of workspace a split-K call needs: 64 KiB of 32-bit arrival counters
+ * (16384, one per row tile; calls with more tiles are refused), then S*M*N
+ * float32 partials. plan == NULL: the default plan. Returns 0 for arguments no
+ * call accepts. */
+size_t skinny_gemm_split_k_workspace_bytes(int M, int N, int K, const skinny_plan_t *plan);
+
+/* Split-K with a caller-owned workspace: a DEVICE pointer, 256-byte aligned, of
+ * at least skinny_gemm_split_k_workspace_bytes() bytes, overlapping none of x, W,
+ * y. Its first 64 KiB (the counters) must be zero before the first call: fill the
+ * workspace with zeros once, when it is allocated. Every complete call leaves the
+ * counters zero again and writes partials only after them, which need no
+ * clearing, so one workspace serves any later call it is large enough for,
+ * eagerly or from a graph replay. Calls that may run at the same time (other
+ * streams) must not share a workspace. Refused (SKINNY_ERR_INVALID_ARG): a
+ * missing, misaligned, too small or overlapping workspace; more than 16384 row
+ * tiles. */
+int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N, int K,
+                             const skinny_plan_t *plan, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* The compiled split-K variants (k_split = 0 in each: S is chosen per call), and
+ * the default plan for a shape. Host-only. */
+int skinny_gemm_split_k_num_variants(void);
+int skinny_gemm_split_k_get_variant(int index, skinny_plan_t *out);
+int skinny_gemm_split_k_default_plan(int M, int N, int K, skinny_plan_t *out);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *skinny_gemm_status_string(int status);

@@ -348,3 +348,93 @@ def test_plan_table_covers_the_decode_shapes():
     assert sorted(cells) == sorted(want)
     for s in want:
         assert cells[s] == set(range(1, 9)), s
+
+
+# ---------------------------------------------------------------------------
+# cross-block split-K: host-side contract (sizes, plans, refusals)
+# ---------------------------------------------------------------------------
+
+def _split_plan(skg, lanes=64, chunks=2, rows=1, S=4, tpb=256, **kw):
+    d = dict(kind=skg.SKINNY_KIND_SPLIT_K, threads_per_block=tpb, lanes_per_row=lanes, chunks=chunks,
+             rows_per_wave=rows, k_split=S, nontemporal=1, grid_blocks=0, x_in_lds=0, prefetch=0)
+    d.update(kw)
+    return skg.Plan(**d)
+
+
+def test_split_k_variants_and_defaults(skg):
+    vs = skg.split_k_variants()
+    assert len(vs) == skg.skinny_gemm_split_k_num_variants() > 0
+    for v in vs:
+        assert v.kind == skg.SKINNY_KIND_SPLIT_K and v.k_split == 0 and v.grid_blocks == 0
+    with pytest.raises(skg.SkinnyError):
+        skg.skinny_gemm_split_k_get_variant(len(vs))
+    # the default: 256 threads, one row per wave, S tried in 4, 2, 8 order
+    for K, lanes, chunks, S in ((4096, 64, 2, 4), (8192, 64, 4, 4), (1024, 64, 1, 2),
+                                (2048, 64, 1, 4), (1536, 32, 3, 2)):
+        p = skg.skinny_gemm_split_k_default_plan(1, 4096, K)
+        assert (p.lanes_per_row, p.chunks, p.rows_per_wave, p.k_split, p.threads_per_block) == \
+            (lanes, chunks, 1, S, 256), K
+        assert S * lanes * 8 * chunks == K
+    for K in (1000, 12288, 8):
+        with pytest.raises(skg.SkinnyError) as e:
+            skg.skinny_gemm_split_k_default_plan(1, 4096, K)
+        assert e.value.status == skg.SKINNY_ERR_UNSUPPORTED
+
+
+def test_split_k_workspace_bytes(skg):
+    """64 KiB of tile counters, then S*M*N float partials."""
+    for M, N, K, tpb, rows, lanes, chunks, S in ((1, 4096, 4096, 256, 1, 64, 2, 4),
+                                                 (4, 1000, 4096, 256, 2, 64, 4, 2),
+                                                 (8, 77, 1536, 64, 1, 32, 3, 2)):
+        p = _split_plan(skg, lanes, chunks, rows, S, tpb)
+        assert skg.skinny_gemm_split_k_workspace_bytes(M, N, K, p) == 65536 + S * M * N * 4
+    # 16384 tiles at most: 4 rows per tile at 256 threads, one row per wave
+    assert skg.skinny_gemm_split_k_workspace_bytes(1, 4 * 16384, 4096, _split_plan(skg)) > 0
+    assert skg.skinny_gemm_split_k_workspace_bytes(1, 4 * 16384 + 1, 4096, _split_plan(skg)) == 0
+    # refused: M out of range, K not S * slice, bad plan fields
+    assert skg.skinny_gemm_split_k_workspace_bytes(9, 4096, 4096, None) == 0
+    assert skg.skinny_gemm_split_k_workspace_bytes(0, 4096, 4096, None) == 0
+    assert skg.skinny_gemm_split_k_workspace_bytes(1, 4096, 2048, _split_plan(skg)) == 0
+    for bad in (dict(grid_blocks=4), dict(x_in_lds=1), dict(prefetch=1), dict(nontemporal=0),
+                dict(tpb=96), dict(tpb=1024), dict(S=0), dict(kind=1), dict(chunks=5)):
+        kw = dict(bad)
+        tpb = kw.pop("tpb", 256)
+        S = kw.pop("S", 4)
+        assert skg.skinny_gemm_split_k_workspace_bytes(1, 4096, 4096, _split_plan(skg, S=S, tpb=tpb, **kw)) == 0, bad
+
+
+def test_split_k_refusals_need_no_device(skg):
+    """Every refusal below is decided before the library looks for a device."""
+    L = skg.lib()
+    x, W, y, ws = 0x10000000, 0x20000000, 0x30000000, 0x40000000  # never dereferenced
+    M, N, K = 2, 1024, 4096
+    p = _split_plan(skg)
+    need = skg.skinny_gemm_split_k_workspace_bytes(M, N, K, p)
+    E = skg.SKINNY_ERR_INVALID_ARG
+    call = L.skinny_gemm_bf16_split_k
+    r = ctypes.byref
+    assert call(x, W, y, M, N, K, r(p), ws, need - 1, None) == E      # workspace too small
+    assert call(x, W, y, M, N, K, r(p), None, need, None) == E        # no workspace
+    assert call(x, W, y, M, N, K, r(p), ws + 128, need, None) == E    # not 256-byte aligned
+    assert call(x, W, y, M, N, K, r(p), y, need, None) == E           # workspace over y
+    assert call(x, W, y, M, N, K, r(p), W - 256, need, None) == E     # workspace over W
+    assert call(x, W, y, M, N, 2048, r(p), ws, need, None) == E       # K != S * slice
+    assert call(x + 8, W, y, M, N, K, r(p), ws, need, None) == E      # x not 16-byte aligned
+    assert call(x, W, y, M, N, K - 4, None, ws, need, None) == E      # K % 8 != 0
+    assert call(x, W, y, 9, N, K, None, ws, need, None) == E          # M > 8
+    assert call(x, W, y, M, N, 0, None, ws, need, None) == E          # K == 0
+    assert call(x, W, None, M, N, K, r(p), ws, need, None) == E       # no y
+    assert call(x, W, x, M, N, K, r(p), ws, need, None) == E          # y over x
+    # nothing to do: M == 0 or N == 0 is a no-op with any pointers
+    assert call(None, None, None, 0, N, K, None, None, 0, None) == skg.SKINNY_OK
+    assert call(None, None, None, M, 0, K, None, None, 0, None) == skg.SKINNY_OK
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-device path")
+def test_split_k_no_device(skg):
+    L = skg.lib()
+    p = _split_plan(skg)
+    need = skg.skinny_gemm_split_k_workspace_bytes(2, 1024, 4096, p)
+    st = L.skinny_gemm_bf16_split_k(0x10000000, 0x20000000, 0x30000000, 2, 1024, 4096, ctypes.byref(p),
+                                    0x40000000, need, None)
+    assert st in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
