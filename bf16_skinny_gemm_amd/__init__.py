@@ -15,11 +15,11 @@ Python ints; a non-zero status raises :class:`SkinnyError`):
     skinny_gemm_num_variants, skinny_gemm_get_variant,
     skinny_gemm_status_string, skinny_gemm_version,
     skinny_gemm_split_k_workspace_bytes, skinny_gemm_bf16_split_k,
-    skinny_gemm_split_k_num_variants,
+    skinny_gemm_bf16_split_k_noalloc, skinny_gemm_split_k_num_variants,
     skinny_gemm_split_k_get_variant, skinny_gemm_split_k_default_plan
 
 Tensor helpers: :func:`gemm`, :func:`gemm_pair`, :func:`gemm_pair_strided`,
-:func:`split_k_workspace` and :func:`gemm_split_k`.
+:func:`split_k_workspace`, :func:`gemm_split_k` and :func:`gemm_split_k_noalloc`.
 """
 from __future__ import annotations
 
@@ -114,6 +114,7 @@ def lib() -> ctypes.CDLL:
         L.skinny_gemm_split_k_workspace_bytes.argtypes = [i, i, i, pp]
         L.skinny_gemm_split_k_workspace_bytes.restype = ctypes.c_size_t
         L.skinny_gemm_bf16_split_k.argtypes = [vp, vp, vp, i, i, i, pp, vp, ctypes.c_size_t, vp]
+        L.skinny_gemm_bf16_split_k_noalloc.argtypes = [vp, vp, vp, i, i, i, pp, vp]
         L.skinny_gemm_split_k_num_variants.argtypes = []
         L.skinny_gemm_split_k_get_variant.argtypes = [i, pp]
         L.skinny_gemm_split_k_default_plan.argtypes = [i, i, i, pp]
@@ -122,7 +123,7 @@ def lib() -> ctypes.CDLL:
                      "skinny_gemm_bf16_f32out_ex", "skinny_gemm_bf16_pair_strided",
                      "skinny_gemm_bf16_pair_strided_ex", "skinny_gemm_get_plan",
                      "skinny_gemm_num_variants", "skinny_gemm_get_variant", "skinny_gemm_version",
-                     "skinny_gemm_bf16_split_k",
+                     "skinny_gemm_bf16_split_k", "skinny_gemm_bf16_split_k_noalloc",
                      "skinny_gemm_split_k_num_variants", "skinny_gemm_split_k_get_variant",
                      "skinny_gemm_split_k_default_plan"):
             getattr(L, name).restype = ctypes.c_int
@@ -236,6 +237,12 @@ def skinny_gemm_bf16_split_k(x: int, W: int, y: int, M: int, N: int, K: int, pla
                              workspace: int, workspace_bytes: int, stream: int = 0) -> None:
     _check(lib().skinny_gemm_bf16_split_k(x, W, y, M, N, K, _plan_ref(plan), workspace,
                                           workspace_bytes, stream), "skinny_gemm_bf16_split_k")
+
+
+def skinny_gemm_bf16_split_k_noalloc(x: int, W: int, y: int, M: int, N: int, K: int,
+                                     plan: Plan | None = None, stream: int = 0) -> None:
+    _check(lib().skinny_gemm_bf16_split_k_noalloc(x, W, y, M, N, K, _plan_ref(plan), stream),
+           "skinny_gemm_bf16_split_k_noalloc")
 
 
 def skinny_gemm_split_k_num_variants() -> int:
@@ -476,11 +483,22 @@ def gemm_split_k(x: torch.Tensor, W: torch.Tensor, workspace: torch.Tensor,
     return out
 
 
+def gemm_split_k_noalloc(x: torch.Tensor, W: torch.Tensor, plan: Plan | None = None,
+                         out: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x @ W.T with cross-block split-K on the library's static workspace
+    (skinny_gemm_bf16_split_k_noalloc); with `out` given, nothing is allocated."""
+    M, N, K, out = _split_args(x, W, out)
+    s = _stream_handle(x.device)
+    with _on_device(x.device):
+        skinny_gemm_bf16_split_k_noalloc(x.data_ptr(), W.data_ptr(), out.data_ptr(), M, N, K, plan, s)
+    return out
+
+
 __all__ = [
     "SkinnyError", "Plan", "lib", "variants", "gemm", "gemm_pair", "gemm_pair_strided",
-    "split_k_variants", "split_k_workspace", "gemm_split_k",
+    "split_k_variants", "split_k_workspace", "gemm_split_k", "gemm_split_k_noalloc",
     "skinny_gemm_split_k_workspace_bytes", "skinny_gemm_bf16_split_k",
-    "skinny_gemm_split_k_num_variants",
+    "skinny_gemm_bf16_split_k_noalloc", "skinny_gemm_split_k_num_variants",
     "skinny_gemm_split_k_get_variant", "skinny_gemm_split_k_default_plan", "SKINNY_KIND_SPLIT_K",
     "skinny_gemm_bf16_pair_strided", "skinny_gemm_bf16_pair_strided_ex",
     "skinny_gemm_init", "skinny_gemm_bf16", "skinny_gemm_bf16_pair", "skinny_gemm_bf16_ex",

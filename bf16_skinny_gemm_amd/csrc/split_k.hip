@@ -148,6 +148,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void split_k_kernel(SplitArgs a)
         __hip_atomic_store(&a.count[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Sets n words to zero (the counters of the library's static workspace).
+__global__ void clear_words_kernel(unsigned *p, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        p[i] = 0u;
+}
+
 }  // namespace skg
 
 namespace {
@@ -349,6 +357,66 @@ int check_current_device()
     return skinny_gemm_init(dev);
 }
 
+// --- the library's own workspace, for callers that cannot allocate -----------
+
+// Largest partials skinny_gemm_bf16_split_k_noalloc serves: 4 MiB (S*M*N <= 2^20).
+constexpr size_t kScratchPartBytes = (size_t)4 << 20;
+constexpr size_t kScratchBytes = kPartOffset + kScratchPartBytes;
+
+}  // namespace
+
+// One copy per GPU, in the workspace layout above, held from the library's load
+// until the process ends. In host code this name is only a handle for
+// hipGetSymbolAddress: each GPU's copy has its own device address, which that
+// call returns and which is all the kernels are ever given (g_scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<int> g_scratch_state[64];  // per device: 0 not set up, 1 ready, < 0 a status
+void *g_scratch_ptr[64];
+
+// Device address of the current GPU's copy of `scratch`, looked up once per device
+// with that device current. The first lookup also enqueues, on `stream`, a kernel
+// that zeroes the copy's counters (static storage starts at zero; the kernel makes
+// it explicit). Later calls find the counters at zero, as every call leaves them.
+int scratch_ptr(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SKINNY_ERR_UNSUPPORTED;
+    }
+    if (dev < 0 || dev >= 64)
+        return SKINNY_ERR_UNSUPPORTED;
+    int state = g_scratch_state[dev].load(std::memory_order_acquire);
+    if (state == 0) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        state = g_scratch_state[dev].load(std::memory_order_relaxed);
+        if (state == 0) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return SKINNY_ERR_LAUNCH;  // not cached: the next call tries again
+            }
+            unsigned *cnt = static_cast<unsigned *>(p);
+            int n = (int)kCountWords;
+            void *args[] = {&cnt, &n};
+            if (hipLaunchKernel(reinterpret_cast<const void *>(&skg::clear_words_kernel),
+                                dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess) {
+                (void)hipGetLastError();
+                return SKINNY_ERR_LAUNCH;
+            }
+            g_scratch_ptr[dev] = p;
+            state = 1;
+            g_scratch_state[dev].store(state, std::memory_order_release);
+        }
+    }
+    *out = g_scratch_ptr[dev];
+    return SKINNY_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -390,6 +458,27 @@ int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N
     if (st != SKINNY_OK)
         return st;
     return split_launch(c, sc, workspace, stream) == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
+}
+
+int skinny_gemm_bf16_split_k_noalloc(const void *x, const void *W, void *y, int M, int N, int K,
+                                     const skinny_plan_t *plan, hipStream_t stream)
+{
+    const Call c = single_call(x, W, y, M, N, K, 0);
+    SplitCall sc;
+    bool empty = false;
+    int st = split_prepare(c, plan, &sc, &empty);
+    if (st != SKINNY_OK || empty)
+        return st;
+    if (sc.lay.part_bytes > kScratchPartBytes)
+        return SKINNY_ERR_INVALID_ARG;
+    st = check_current_device();
+    if (st != SKINNY_OK)
+        return st;
+    void *ws = nullptr;
+    st = scratch_ptr(stream, &ws);
+    if (st != SKINNY_OK)
+        return st;
+    return split_launch(c, sc, ws, stream) == hipSuccess ? SKINNY_OK : SKINNY_ERR_LAUNCH;
 }
 
 int skinny_gemm_split_k_num_variants(void) { return kNumSplit; }

@@ -242,6 +242,20 @@ int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N
                              const skinny_plan_t *plan, void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Split-K for callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and result as skinny_gemm_bf16_split_k, on the library's own static
+ * workspace instead of a caller's. That workspace is one device array per GPU, in
+ * the same layout (64 KiB of counters, then 4 MiB of partials), held from the
+ * library's load until the process ends; a call whose S*M*N exceeds 2^20, or that
+ * has more than 16384 row tiles, returns SKINNY_ERR_INVALID_ARG. The first call on
+ * a GPU looks up that GPU's copy and enqueues one small kernel on `stream` that
+ * zeroes its counters; no call allocates or frees memory. Every call on a GPU
+ * shares that GPU's copy, so calls that may overlap on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller. */
+int skinny_gemm_bf16_split_k_noalloc(const void *x, const void *W, void *y, int M, int N, int K,
+                                     const skinny_plan_t *plan, hipStream_t stream);
+
 /* The compiled split-K variants (k_split = 0 in each: S is chosen per call), and
  * the default plan for a shape. Host-only. */
 int skinny_gemm_split_k_num_variants(void);

@@ -438,3 +438,18 @@ def test_split_k_no_device(skg):
     st = L.skinny_gemm_bf16_split_k(0x10000000, 0x20000000, 0x30000000, 2, 1024, 4096, ctypes.byref(p),
                                     0x40000000, need, None)
     assert st in (skg.SKINNY_ERR_UNSUPPORTED, skg.SKINNY_ERR_INVALID_ARG)
+
+
+def test_split_k_noalloc_refusals_need_no_device(skg):
+    """The static workspace's limits are checked before any device work."""
+    L = skg.lib()
+    x, W, y = 0x10000000, 0x40000000, 0x80000000  # never dereferenced
+    p = _split_plan(skg)  # S = 4 at K = 4096, 4 rows per tile
+    E = skg.SKINNY_ERR_INVALID_ARG
+    call = L.skinny_gemm_bf16_split_k_noalloc
+    assert call(x, W, y, 8, 32769, 4096, ctypes.byref(p), None) == E  # S*M*N > 2^20
+    assert call(x, W, y, 1, 4 * 16384 + 4, 4096, ctypes.byref(p), None) == E  # > 16384 tiles
+    assert call(x, W, y, 9, 1024, 4096, None, None) == E
+    assert call(x + 8, W, y, 1, 1024, 4096, None, None) == E
+    assert call(x, W, None, 1, 1024, 4096, None, None) == E
+    assert call(None, None, None, 0, 1024, 4096, None, None) == skg.SKINNY_OK
