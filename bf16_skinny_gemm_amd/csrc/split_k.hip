@@ -15,16 +15,22 @@
 // plan with the same (lanes_per_row, chunks, k_split = S).
 //
 // Hand-off between blocks, with no block ever waiting for another:
-//   1. every lane that holds a row sum stores it to part[s][m][row];
-//   2. each thread fences (release, agent scope: its stores reach the device
-//      coherence point, past the per-XCD L2), then the block meets at a barrier;
-//   3. one thread adds 1 to the tile's arrival counter (acq_rel, agent scope);
-//      the block that sees S - 1 there is the last of its tile;
-//   4. the last block fences (acquire, agent scope), adds the S partials of each
-//      of its outputs in slice order, rounds once to bfloat16, stores y, and
-//      sets the counter back to 0.
-// Counters therefore hold 0 between calls; partials are always written before
-// they are read, so they need no clearing.
+//   1. every lane that holds a row sum stores it to part[s][m][row] as an
+//      agent-scope atomic store (on gfx950 a store with the sc1 bit: coherent
+//      across the eight XCDs' L2 caches by itself);
+//   2. each wave waits until its stores are complete (vmcnt 0), then the block
+//      meets at a barrier;
+//   3. one thread adds 1 to the tile's arrival counter (an agent-scope atomic, so
+//      it is issued after every partial of the block is visible device-wide); the
+//      block that sees S - 1 there is the last of its tile;
+//   4. the last block reads the S partials of each of its outputs with agent-scope
+//      atomic loads (sc1: not served by a stale line of its own L2), adds them in
+//      slice order, rounds once to bfloat16, stores y, and sets the counter back
+//      to 0.
+// No fence is used: an agent-scope release or acquire fence writes back or
+// invalidates the whole L2 of the XCD, and with one per block the kernel ran
+// 10-40x slower than the in-block plans. Counters therefore hold 0 between calls;
+// partials are always written before they are read, so they need no clearing.
 #include "skinny_gemm.h"
 
 #include <hip/hip_runtime.h>
@@ -46,6 +52,9 @@ struct SplitArgs {
     unsigned *count;     // [tiles] arrival counters, 0 between calls
     int N, K, splits, tiles;
 };
+
+// s_waitcnt operand (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int M, int LPR, int CH, int R, bool NT>
 __global__ __launch_bounds__(kMaxWaves * 64) void split_k_kernel(SplitArgs a)
@@ -113,34 +122,35 @@ __global__ __launch_bounds__(kMaxWaves * 64) void split_k_kernel(SplitArgs a)
             if (row < a.N) {
 #pragma unroll
                 for (int m = 0; m < M; ++m)
-                    a.part[(size_t)s * plane + (size_t)m * a.N + row] = acc[m][r];
+                    __hip_atomic_store(&a.part[(size_t)s * plane + (size_t)m * a.N + row], acc[m][r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-    // 2.-3. publish them and count this block in
+    // 2.-3. wait for them, then count this block in
     __shared__ int last;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned before =
-            __hip_atomic_fetch_add(&a.count[tile], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&a.count[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = before == (unsigned)(a.splits - 1);
     }
     __syncthreads();
     if (!last)
         return;  // block-uniform
 
-    // 4. the last block of the tile: every other slice's partials are visible now
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // 4. the last block of the tile: every slice's partials are complete
     const int base = tile * rows_t;
     for (int i = (int)threadIdx.x; i < M * rows_t; i += (int)blockDim.x) {
         const int m = i / rows_t;
         const int row = base + (i - m * rows_t);
         if (row < a.N) {
             const size_t o = (size_t)m * a.N + row;
-            float v = a.part[o];
+            float v = __hip_atomic_load(&a.part[o], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             for (int q = 1; q < a.splits; ++q)
-                v += a.part[(size_t)q * plane + o];
+                v += __hip_atomic_load(&a.part[(size_t)q * plane + o], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             a.y[o] = f32_to_bf16(v);
         }
     }

@@ -133,6 +133,22 @@ def rotated_order(n: int, rnd: int) -> list:
     return [k] + (rest[::-1] if rnd % 2 else rest)
 
 
+def split_k_plans(skg, K, M, N):
+    """Every cross-block split-K plan able to run (K, M): each compiled variant at
+    the slice count that makes K, block sizes 64..512."""
+    out = []
+    for v in skg.split_k_variants():
+        d = v.as_dict()
+        slice_k = d["lanes_per_row"] * 8 * d["chunks"]
+        if K % slice_k or K // slice_k > 16:
+            continue
+        for tpb in (64, 128, 256, 512):
+            p = skg.Plan.from_dict({**d, "threads_per_block": tpb, "k_split": K // slice_k})
+            if skg.skinny_gemm_split_k_workspace_bytes(M, N, K, p):
+                out.append(p)
+    return out
+
+
 def candidate_plans(skg, K, M, kinds=None, grids=(0, BIG_GRID)):
     """Every (variant, block size, grid mode) able to run (K, M)."""
     out = []
@@ -161,9 +177,15 @@ def plan_key(p) -> tuple:
 
 def time_plan(torch, skg, x, weights, ys, plan, pair, trials, replays):
     """Median microseconds per call over graph replays of one call per weight copy."""
+    ws = None
+    if plan.kind == skg.SKINNY_KIND_SPLIT_K:  # one workspace serves the calls in turn
+        ws = skg.split_k_workspace(x.shape[0], weights[0].shape[0], x.shape[1], plan, device=x.device)
+
     def run():
         for w in weights:
-            if pair:
+            if ws is not None:
+                skg.gemm_split_k(x, w, ws, plan=plan, out=ys)
+            elif pair:
                 skg.gemm_pair(x, w[0], w[1], out0=ys[0], out1=ys[1], plan=plan)
             else:
                 skg.gemm(x, w, out=ys, plan=plan)
@@ -315,8 +337,11 @@ def measure(args):
                 best = None
                 kinds = {int(k) for k in args.kinds.split(",")} if args.kinds else None
                 grids = None if args.grids == "same" else parse_grids(args.grids)
-                plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids, args.twins)
-                         if args.refine else candidate_plans(skg, K, M, kinds, grids))
+                if kinds == {skg.SKINNY_KIND_SPLIT_K}:
+                    plans = [] if pair else split_k_plans(skg, K, M, N)
+                else:
+                    plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids, args.twins)
+                             if args.refine else candidate_plans(skg, K, M, kinds, grids))
                 current = None
                 if args.with_table and (N, K, M) in table:
                     # the table's plan for the cell runs first and is always a finalist,
@@ -394,7 +419,7 @@ def emit_inc(paths, out=INC_PATH):
         with open(path) as f:
             for line in f:
                 r = json.loads(line)
-                if "plan" not in r:
+                if "plan" not in r or r["plan"]["kind"] == 5:  # split-K: not for the table
                     continue
                 mine.setdefault((r["N"], r["K"], r["M"]), []).append(r)
         recs.update(mine)
@@ -419,12 +444,41 @@ def emit_inc(paths, out=INC_PATH):
     return out
 
 
+def split_k_report(path) -> str:
+    """Per cell of a `--kinds 5 --with-table` sweep: the table's plan against the
+    fastest split-K plan, both from the same rounds (stage 2 when timed in rounds)."""
+    by = {}
+    with open(path) as f:
+        for line in f:
+            r = json.loads(line)
+            if "plan" in r:
+                by.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+    rows = ["| (N, K) | M | table plan µs | best split-K µs | split-K ÷ table | split-K plan "
+            "(lanes, chunks, rows/wave, S, threads) |", "|---|---|---|---|---|---|"]
+    for (N, K, M) in sorted(by):
+        rs = by[(N, K, M)]
+        final = [r for r in rs if r.get("stage") == 2] or rs
+        table = [r for r in final if r["plan"]["kind"] != 5]
+        split = [r for r in final if r["plan"]["kind"] == 5] or [r for r in rs if r["plan"]["kind"] == 5]
+        if not table or not split:
+            continue
+        t = min(r["us"] for r in table)
+        b = min(split, key=lambda r: r["us"])
+        p = b["plan"]
+        rows.append(f"| ({N},{K}) | {M} | {t:.3f} | {b['us']:.3f} | {b['us'] / t:.2f} | "
+                    f"({p['lanes_per_row']}, {p['chunks']}, {p['rows_per_wave']}, {p['k_split']}, "
+                    f"{p['threads_per_block']}) |")
+    return "\n".join(rows)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--out", help="JSON-lines file to append measurements to")
     ap.add_argument("--emit-inc", metavar="JSONL[,JSONL...]",
                     help="write the plan table from sweep files (records pooled)")
     ap.add_argument("--inc-path", default=INC_PATH)
+    ap.add_argument("--split-k-report", metavar="JSONL",
+                    help="print table-plan vs split-K times per cell of a --kinds 5 --with-table sweep")
     ap.add_argument("--only", help="comma list of NxK shapes to sweep")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
     ap.add_argument("--kinds", help="comma list of plan kinds to time (default: all)")
@@ -450,6 +504,9 @@ def main():
     ap.add_argument("--trials", type=int, default=3)
     ap.add_argument("--replays", type=int, default=5)
     args = ap.parse_args()
+    if args.split_k_report:
+        print(split_k_report(args.split_k_report))
+        return 0
     if args.emit_inc:
         print(emit_inc(args.emit_inc, args.inc_path))
         return 0

@@ -205,10 +205,10 @@ int skinny_gemm_get_variant(int index, skinny_plan_t *out);
  * (plan.k_split) that S different blocks take: the single-launch form of the
  * split-K + reduce kernel pair that vLLM PR #65306 (SM90 skinny GEMM plans),
  * section Details, counts against cuBLAS on its small-N / large-K shapes. Each
- * block stores its float32 partial sums in a workspace, and the last block of a
- * row tile to arrive (a per-tile arrival counter, agent-scope release/acquire)
- * adds the S partials in slice order 0..S-1 and writes bfloat16 y. No block waits
- * for another. The result equals, bit for bit, that of the FIXED_K plan with the
+ * block stores its float32 partial sums in a workspace with device-coherent
+ * stores, waits for them and bumps a per-tile arrival counter; the last block of
+ * a row tile to arrive reads the S partials with device-coherent loads, adds them
+ * in slice order 0..S-1 and writes bfloat16 y. No block waits for another. The result equals, bit for bit, that of the FIXED_K plan with the
  * same (lanes_per_row, chunks) and k_split = S.
  *
  * Plans: kind SKINNY_KIND_SPLIT_K, a variant from skinny_gemm_split_k_get_variant

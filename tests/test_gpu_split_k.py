@@ -66,7 +66,7 @@ def nan_fill(t: torch.Tensor) -> None:
 
 
 # ---------------------------------------------------------------------------
-# every split-K variant, every M, S = 1, 2, 4, 8, several tiles and a ragged tail
+# every split-K variant, every M, S = 1..16, several tiles and a ragged tail
 # ---------------------------------------------------------------------------
 
 def _variants():
@@ -83,7 +83,7 @@ def _variants():
 def test_every_split_variant(skg, variant):
     assert variant is not None, "library missing"
     ran = 0
-    for S in (1, 2, 4, 8):
+    for S in (1, 2, 4, 8, 16):
         K = S * variant.lanes_per_row * 8 * variant.chunks
         for tpb in (256, 64):
             rows_t = tpb // 64 * variant.rows_per_wave * (64 // variant.lanes_per_row)

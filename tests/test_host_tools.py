@@ -393,3 +393,28 @@ def test_bench_tables_render_a_line():
     assert "1400.0 µs per step of 186 calls" in out and "| (4096,4096) | 34 | `k(skg::Args)` | 6.700 | 62.6 |" in out
     assert "| (4096,4096)M1 | 7.000 (6.900) | 60.0 | 6.690 | 62.7 |" in out
     assert "| 1 | 1.56 | n/a |" in out
+
+
+def test_split_k_report(tmp_path):
+    """Table plan vs fastest split-K plan per cell, from the round records when present."""
+    from bf16_skinny_gemm_amd import sweep
+
+    def rec(M, kind, us, stage=None, S=0):
+        plan = {"kind": kind, "threads_per_block": 256, "lanes_per_row": 64, "chunks": 2,
+                "rows_per_wave": 1, "k_split": S, "nontemporal": 1, "grid_blocks": 0,
+                "x_in_lds": 0, "prefetch": 0}
+        r = {"N": 2048, "K": 4096, "M": M, "pair": False, "plan": plan, "us": us}
+        if stage:
+            r["stage"] = stage
+        return json.dumps(r)
+
+    lines = [rec(1, 1, 4.4, 1), rec(1, 5, 5.0, 1, S=4), rec(1, 5, 3.0, 1, S=8),  # single pass
+             rec(1, 1, 4.5, 2), rec(1, 5, 5.9, 2, S=4),                        # rounds decide
+             rec(2, 1, 4.7), rec(2, 5, 6.0, S=2),
+             json.dumps({"N": 2048, "K": 4096, "M": 2, "pair": False, "complete": True})]
+    p = tmp_path / "s.jsonl"
+    p.write_text("\n".join(lines) + "\n")
+    out = sweep.split_k_report(str(p)).splitlines()
+    assert out[2] == "| (2048,4096) | 1 | 4.500 | 5.900 | 1.31 | (64, 2, 1, 4, 256) |"
+    assert out[3] == "| (2048,4096) | 2 | 4.700 | 6.000 | 1.28 | (64, 2, 1, 2, 256) |"
+    assert len(out) == 4
