@@ -22,9 +22,11 @@
  *    [M][N]. No bias, no scaling.
  *  - The caller owns every buffer. The library never allocates, frees or
  *    synchronises in a compute call; it enqueues exactly one kernel on
- *    `stream` (0 = the null stream) and returns. Calls are therefore legal
- *    inside HIP graph capture. y must not overlap x or W (or, for the pair,
- *    each other).
+ *    `stream` (0 = the null stream) and returns (the first allocation-free
+ *    split-K call on a GPU enqueues one more, see below). Calls are therefore
+ *    legal inside HIP graph capture. y must not overlap x or W (or, for the
+ *    pair, each other). The only device memory the library owns is the static
+ *    split-K workspace of skinny_gemm_bf16_split_k_noalloc, one per GPU.
  *  - Sizes: 0 <= M <= 8; N >= 0; K >= 0. M == 0 or N == 0 is a no-op that
  *    returns SKINNY_OK (pointers may then be NULL). K == 0 writes +0 to all of
  *    y (the empty sum). M = 1..4 is the decode range the cited plans cover;
@@ -45,11 +47,13 @@
  *    share those give identical bits, and the pair gives the same bits as two
  *    single calls with the same plan.
  *  - Thread safety: every entry point may be called from any host thread; the
- *    only shared state is host-side caches filled on first use under a lock or
+ *    only shared host state is caches filled on first use under a lock or
  *    with atomics (device properties; per kernel, its occupancy, static LDS
  *    size and raised LDS limit; per (device, N, K, M, single or pair), the
  *    resolved launch of the default plan, written once and then read without
- *    a lock, so that a repeated call does no table lookup).
+ *    a lock, so that a repeated call does no table lookup; per device, the
+ *    address of the static split-K workspace). Device-side, split-K calls that
+ *    share a workspace (a caller's, or the static one) must not overlap.
  */
 #ifndef SKINNY_GEMM_H
 #define SKINNY_GEMM_H
