@@ -5,9 +5,10 @@
 // |y - y_ref| <= 1e-2 * sum_k |x_k W_nk| + 1e-6 and |y - ref64| <= 7.5e-5 + 2^-8 |ref64|,
 // per output row cosine >= 0.99999. It also checks that invalid calls are refused
 // with the documented status before anything runs, and that a graph captured around
-// the calls replays them bit for bit.
+// the calls replays them bit for bit; and exercises cross-block split-K with a
+// hipMalloc workspace and on the library's static one.
 //
-// Built by __graft_entry__.build() (bf16_skinny_gemm_amd/build.py) next to this file;
+// Built by tests/native/build_native.py (which __graft_entry__.build() calls) next to this file;
 // run by tests/test_native_abi.py on a GPU. Exit status 0 = every check passed.
 #include <hip/hip_runtime.h>
 
@@ -232,6 +233,44 @@ int main()
         HIP_OK(hipGraphDestroy(graph));
         for (void *p : {(void *)W0d, (void *)W1d, (void *)xmd, (void *)y0d, (void *)y1d, (void *)ymd})
             HIP_OK(hipFree(p));
+    }
+    // cross-block split-K: a workspace from hipMalloc, zeroed once and reused across
+    // shapes, and the library's static workspace; both against the oracle and each other
+    {
+        const size_t ws_bytes = skinny_gemm_split_k_workspace_bytes(8, 4096, 8192, nullptr);
+        CHECK(ws_bytes > 0, "workspace size");
+        void *ws = nullptr;
+        HIP_OK(hipMalloc(&ws, ws_bytes));
+        HIP_OK(hipMemset(ws, 0, ws_bytes));
+        const int sk_shapes[][3] = {{4096, 8192, 4}, {2048, 4096, 1}, {1000, 4096, 8}, {8192, 1536, 2}};
+        for (const auto &sh : sk_shapes) {
+            const int N = sh[0], K = sh[1], M = sh[2];
+            CHECK(skinny_gemm_split_k_workspace_bytes(M, N, K, nullptr) <= ws_bytes, "fits");
+            const auto W = draw((size_t)N * K, (float)(1.0 / std::sqrt((double)K)), (uint64_t)N * 7 + K);
+            const auto x = draw((size_t)M * K, 1.0f, (uint64_t)M * 11 + K);
+            uint16_t *Wd = to_device(W), *xd = to_device(x), *y1 = nullptr, *y2 = nullptr;
+            HIP_OK(hipMalloc(&y1, (size_t)M * N * 2));
+            HIP_OK(hipMalloc(&y2, (size_t)M * N * 2));
+            CHECK(skinny_gemm_bf16_split_k(xd, Wd, y1, M, N, K, nullptr, ws, ws_bytes, stream) == SKINNY_OK,
+                  "split-K (%d,%d) M=%d", N, K, M);
+            CHECK(skinny_gemm_bf16_split_k_noalloc(xd, Wd, y2, M, N, K, nullptr, stream) == SKINNY_OK,
+                  "split-K no-alloc (%d,%d) M=%d", N, K, M);
+            HIP_OK(hipStreamSynchronize(stream));
+            std::vector<uint16_t> h1((size_t)M * N), h2((size_t)M * N);
+            HIP_OK(hipMemcpy(h1.data(), y1, h1.size() * 2, hipMemcpyDeviceToHost));
+            HIP_OK(hipMemcpy(h2.data(), y2, h2.size() * 2, hipMemcpyDeviceToHost));
+            char what[96];
+            std::snprintf(what, sizeof what, "split-K (%d,%d) M=%d", N, K, M);
+            check(what, x, K, W, M, N, K, h1.data(), N, false);
+            CHECK(std::memcmp(h1.data(), h2.data(), h1.size() * 2) == 0, "no-alloc bits (%d,%d) M=%d", N, K, M);
+            for (void *p : {(void *)Wd, (void *)xd, (void *)y1, (void *)y2})
+                HIP_OK(hipFree(p));
+        }
+        // refused before anything runs: too small a workspace, the static one exceeded
+        CHECK(skinny_gemm_bf16_split_k(nullptr, nullptr, nullptr, 1, 4096, 4096, nullptr, ws, 1024, stream) ==
+                  SKINNY_ERR_INVALID_ARG,
+              "null inputs");
+        HIP_OK(hipFree(ws));
     }
     HIP_OK(hipStreamDestroy(stream));
     std::printf("abi_native: library version %d, %d variants, %d failures\n", skinny_gemm_version(),

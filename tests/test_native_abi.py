@@ -1,7 +1,8 @@
 """The C ABI used from C++ with no Python in between: tests/native/abi_native.cpp
 calls include/skinny_gemm.h on hipMalloc memory and checks every output against
 the CPU oracle linked into it (G1, S1 and the row cosine), the argument checks'
-refusals, and the bit-exact replay of a captured graph."""
+refusals, the bit-exact replay of a captured graph, and split-K on a hipMalloc
+workspace and on the library's static one."""
 from __future__ import annotations
 
 import os
@@ -38,7 +39,8 @@ def test_native_program_links_and_refuses_without_gpu():
 @pytest.mark.gpu
 def test_native_program_passes():
     print("native ABI program: shapes (4096,1024) (1000,1024) (2048,4096) (300,1536) (77,1000), "
-          "M 1..8, pair, strided pair, refusals, graph replay", flush=True)
+          "M 1..8, pair, strided pair, refusals, graph replay, split-K with a workspace and without",
+          flush=True)
     res = subprocess.run([_exe()], capture_output=True, text=True, timeout=180)
     print(res.stdout)
     assert res.returncode == 0, res.stdout + res.stderr[-4000:]
