@@ -117,3 +117,50 @@ def test_noalloc_refuses_beyond_its_workspace(skg):
     assert noalloc(skg, x, W[:32768], y[:, :32768].contiguous(), plan) == skg.SKINNY_OK
     assert noalloc(skg, x, W, y, plan) == skg.SKINNY_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+_CAPTURE_FIRST = r"""
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+import bf16_skinny_gemm_amd as skg
+dev = torch.device("cuda:0")
+torch.cuda.set_device(dev)
+g0 = torch.Generator(device=dev).manual_seed(23)
+N, K, M = 2048, 4096, 2
+W = (torch.randn(N, K, device=dev, generator=g0) / 64).to(torch.bfloat16)
+x = torch.randn(M, K, device=dev, generator=g0).to(torch.bfloat16)
+y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+g = torch.cuda.CUDAGraph()
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        st = skg.lib().skinny_gemm_bf16_split_k_noalloc(x.data_ptr(), W.data_ptr(), y.data_ptr(),
+                                                        M, N, K, None, s.cuda_stream)
+assert st == 0, st
+torch.cuda.current_stream().wait_stream(s)
+ref = skg.gemm_split_k(x, W, skg.split_k_workspace(M, N, K))
+for r in range(3):
+    y.view(torch.int16).fill_(0x7FC0)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), r
+print("ok")
+"""
+
+
+def test_noalloc_first_call_inside_graph_capture(skg):
+    """A fresh process whose first no-alloc call is made under graph capture (its
+    set-up, the workspace lookup and the counter-clearing kernel, lands in the
+    graph): every replay gives the workspace entry point's bits."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print("fresh process: first no-alloc call under capture, (2048,4096) M=2", flush=True)
+    res = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True, text=True,
+                         timeout=240)
+    assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr[-3000:]
