@@ -1,7 +1,7 @@
 """CPU sanitizer builds: the oracle and the C ABI's host-side argument checks
 compiled with -fsanitize=address,undefined (gcc / g++, host code only) and run
 over random and extreme inputs (tests/sanitize/). Any memory error or undefined
-behaviour aborts the driver (-fno-sanitize-recover=all)."""
+behaviour aborts the fuzzing program (-fno-sanitize-recover=all)."""
 from __future__ import annotations
 
 import os
