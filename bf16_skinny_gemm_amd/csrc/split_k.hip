@@ -253,45 +253,24 @@ bool default_split(int K, int M, skinny_plan_t *out)
     return false;
 }
 
+static_assert(kSplitMaxThreads == skg::kMaxWaves * 64, "split-K block limit");
+
 int split_plan_ok(const skinny_plan_t &p, const SplitVariant *v, int K, int M)
 {
     if (p.kind != SKINNY_KIND_SPLIT_K)
         return SKINNY_ERR_INVALID_ARG;
     if (!v)
         return SKINNY_ERR_UNSUPPORTED;
-    const int tpb = p.threads_per_block;
-    if (tpb < 64 || tpb > skg::kMaxWaves * 64 || tpb % 64 != 0)
-        return SKINNY_ERR_INVALID_ARG;
-    if (p.k_split < 1 || p.k_split > 64 || p.nontemporal != 1 || p.grid_blocks != 0 || p.x_in_lds != 0 ||
-        p.prefetch != 0)
-        return SKINNY_ERR_INVALID_ARG;
-    if (K != v->slice_k * p.k_split)
+    if (!split_fields_ok(p) || K != v->slice_k * p.k_split)
         return SKINNY_ERR_INVALID_ARG;
     if (!v->fn[M - 1])
         return SKINNY_ERR_UNSUPPORTED;
     return SKINNY_OK;
 }
 
-// Workspace layout, the same for every call: kCountWords 32-bit arrival counters
-// (tile t uses word t) in the first 64 KiB, then the float partials [S][M][N].
-// Counters stay at zero between calls and no call writes partials over them, so
-// one workspace serves calls of any shape it is large enough for.
-constexpr size_t kCountWords = 16384;
-constexpr size_t kPartOffset = kCountWords * 4;
-
-struct SplitLayout {
-    size_t part_bytes, total;
-    int tiles;
-};
-
-SplitLayout split_layout(const skinny_plan_t &p, const SplitVariant *v, int M, int N)
+SplitLayout layout_of(const skinny_plan_t &p, const SplitVariant *v, int M, int N)
 {
-    SplitLayout l{};
-    const int rows_t = (p.threads_per_block / 64) * v->rows_per_group;
-    l.tiles = (int)(((long long)N + rows_t - 1) / rows_t);
-    l.part_bytes = (size_t)p.k_split * (size_t)M * (size_t)N * 4;
-    l.total = kPartOffset + l.part_bytes;
-    return l;
+    return split_layout(p.threads_per_block, v->rows_per_group, p.k_split, M, N);
 }
 
 // A resolved split-K call: plan, variant and layout, all checked.
@@ -313,7 +292,7 @@ int split_prepare(const Call &c, const skinny_plan_t *plan_in, SplitCall *out, b
         *empty = true;
         return SKINNY_OK;
     }
-    if (c.K == 0 || !vector_ok(c) || !out_span_ok(c))
+    if (!split_call_ok(c))
         return SKINNY_ERR_INVALID_ARG;
     skinny_plan_t p;
     if (plan_in) {
@@ -330,8 +309,8 @@ int split_prepare(const Call &c, const skinny_plan_t *plan_in, SplitCall *out, b
         return SKINNY_ERR_INVALID_ARG;
     out->plan = p;
     out->v = v;
-    out->lay = split_layout(p, v, c.M, c.N);
-    if ((size_t)out->lay.tiles > kCountWords)
+    out->lay = layout_of(p, v, c.M, c.N);
+    if (!split_layout_ok(out->lay, p.k_split))
         return SKINNY_ERR_INVALID_ARG;
     return SKINNY_OK;
 }
@@ -343,11 +322,11 @@ hipError_t split_launch(const Call &c, const SplitCall &sc, void *workspace, hip
     a.w = static_cast<const uint16_t *>(c.w0);
     a.y = static_cast<uint16_t *>(c.y0);
     a.count = static_cast<unsigned *>(workspace);
-    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kPartOffset);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + kSplitPartOffset);
     a.N = c.N;
     a.K = c.K;
     a.splits = sc.plan.k_split;
-    a.tiles = sc.lay.tiles;
+    a.tiles = (int)sc.lay.tiles;
     void *args[] = {&a};
     const long long grid = (long long)sc.lay.tiles * sc.plan.k_split;
     const hipError_t e = hipLaunchKernel(sc.v->fn[c.M - 1], dim3((unsigned)grid),
@@ -371,7 +350,7 @@ int check_current_device()
 
 // Largest partials skinny_gemm_bf16_split_k_noalloc serves: 4 MiB (S*M*N <= 2^20).
 constexpr size_t kScratchPartBytes = (size_t)4 << 20;
-constexpr size_t kScratchBytes = kPartOffset + kScratchPartBytes;
+constexpr size_t kScratchBytes = kSplitPartOffset + kScratchPartBytes;
 
 }  // namespace
 
@@ -411,7 +390,7 @@ int scratch_ptr(hipStream_t stream, void **out)
                 return SKINNY_ERR_LAUNCH;  // not cached: the next call tries again
             }
             unsigned *cnt = static_cast<unsigned *>(p);
-            int n = (int)kCountWords;
+            int n = (int)kSplitCountWords;
             void *args[] = {&cnt, &n};
             if (hipLaunchKernel(reinterpret_cast<const void *>(&skg::clear_words_kernel),
                                 dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess) {
@@ -444,8 +423,8 @@ size_t skinny_gemm_split_k_workspace_bytes(int M, int N, int K, const skinny_pla
     const SplitVariant *v = find_split(p);
     if (split_plan_ok(p, v, K, M) != SKINNY_OK)
         return 0;
-    const SplitLayout l = split_layout(p, v, M, N);
-    return (size_t)l.tiles > kCountWords ? 0 : l.total;
+    const SplitLayout l = layout_of(p, v, M, N);
+    return split_layout_ok(l, p.k_split) ? l.total : 0;
 }
 
 int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N, int K,
@@ -458,11 +437,7 @@ int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N
     int st = split_prepare(c, plan, &sc, &empty);
     if (st != SKINNY_OK || empty)
         return st;
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < sc.lay.total)
-        return SKINNY_ERR_INVALID_ARG;
-    const size_t xb = span(M, K, K, 2), wb = (size_t)N * K * 2, yb = (size_t)M * N * 2;
-    if (overlaps(workspace, sc.lay.total, x, xb) || overlaps(workspace, sc.lay.total, W, wb) ||
-        overlaps(workspace, sc.lay.total, y, yb))
+    if (!split_workspace_ok(c, workspace, workspace_bytes, sc.lay))
         return SKINNY_ERR_INVALID_ARG;
     st = check_current_device();
     if (st != SKINNY_OK)

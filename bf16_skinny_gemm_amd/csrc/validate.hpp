@@ -115,4 +115,63 @@ inline uint64_t cache_key(int dev, const Call &c)
            ((uint64_t)(c.M - 1) << 52) | ((uint64_t)c.K << 31) | (uint64_t)c.N;
 }
 
+// ---- cross-block split-K (split_k.hip): the checks and the workspace layout ----
+
+// Largest block of the split-K kernels, in threads (8 waves).
+constexpr int kSplitMaxThreads = 512;
+// Workspace layout, the same for every call: kSplitCountWords 32-bit arrival
+// counters (tile t uses word t) in the first 64 KiB, then the float partials
+// [S][M][N]. Counters stay at zero between calls and no call writes partials over
+// them, so one workspace serves calls of any shape it is large enough for.
+constexpr size_t kSplitCountWords = 16384;
+constexpr size_t kSplitPartOffset = kSplitCountWords * 4;
+
+struct SplitLayout {
+    size_t part_bytes, total;
+    long long tiles;
+};
+
+// Row tiles and workspace bytes of a call: tiles of (threads / 64) * rows_per_group
+// rows, S * M * N float partials after the counters.
+inline SplitLayout split_layout(int threads, int rows_per_group, int S, int M, int N)
+{
+    SplitLayout l{};
+    const long long rows_t = (long long)(threads / 64) * rows_per_group;
+    l.tiles = ((long long)N + rows_t - 1) / rows_t;
+    l.part_bytes = (size_t)S * (size_t)M * (size_t)N * 4;
+    l.total = kSplitPartOffset + l.part_bytes;
+    return l;
+}
+
+// The plan fields a split-K plan must hold, apart from which variant it names and
+// whether its slices make K (the caller checks those against the compiled set).
+inline bool split_fields_ok(const skinny_plan_t &p)
+{
+    const int t = p.threads_per_block;
+    return p.kind == SKINNY_KIND_SPLIT_K && t >= 64 && t <= kSplitMaxThreads && t % 64 == 0 &&
+           p.k_split >= 1 && p.k_split <= 64 && p.nontemporal == 1 && p.grid_blocks == 0 &&
+           p.x_in_lds == 0 && p.prefetch == 0;
+}
+
+// A split-K call beyond validate(): K > 0 and the vector path's conditions (there
+// is no element-wise split-K kernel).
+inline bool split_call_ok(const Call &c) { return c.K > 0 && vector_ok(c) && out_span_ok(c); }
+
+// The layout fits the counters, and every block and wave index stays inside int.
+inline bool split_layout_ok(const SplitLayout &l, int S)
+{
+    return l.tiles >= 1 && (size_t)l.tiles <= kSplitCountWords && l.tiles * (long long)S <= 0x7FFFFFFFLL;
+}
+
+// A caller's workspace: present, 256-byte aligned, large enough for the layout and
+// sharing no byte with x, W or y.
+inline bool split_workspace_ok(const Call &c, const void *ws, size_t bytes, const SplitLayout &l)
+{
+    if (!ws || !aligned(ws, 256) || bytes < l.total)
+        return false;
+    const size_t xb = span(c.M, c.K, c.ldx, 2), wb = (size_t)c.N * c.K * 2;
+    const size_t yb = span(c.M, c.N, c.ldy, c.out_f32 ? 4 : 2);
+    return !overlaps(ws, l.total, c.x, xb) && !overlaps(ws, l.total, c.w0, wb) && !overlaps(ws, l.total, c.y0, yb);
+}
+
 }  // namespace skg_host

@@ -9,7 +9,9 @@
 // share a byte, checked byte by byte; the strided-pair test must also accept
 // every pair of output views that is in fact disjoint. Then large and extreme
 // sizes (up to INT_MAX, pointers up to 2^47) run through every check so that
-// the undefined-behaviour sanitizer sees the overflow-prone arithmetic.
+// the undefined-behaviour sanitizer sees the overflow-prone arithmetic. The
+// split-K checks (plan fields, workspace layout, a caller's workspace) run the
+// same way.
 #include <climits>
 #include <cstdio>
 #include <cstdlib>
@@ -183,8 +185,55 @@ int main()
                     }
     EXPECT((long)keys.size() == nkeys, "cache key collision: %zu distinct of %ld", keys.size(), nkeys);
 
+    // cross-block split-K: plan fields, layout and a caller's workspace. When the
+    // checks accept a call, the workspace bytes the kernel touches (counters, then
+    // partials) share no byte with x, W or y, lie inside the given workspace, and the
+    // tiles cover N exactly; random plan fields are accepted only inside their ranges.
+    long split_accepted = 0;
+    for (int it = 0; it < 20000; ++it) {
+        const int M = rnd(1, kMaxM), N = rnd(1, 600), K = 8 * rnd(1, 64);
+        const uintptr_t x = 0x10000 + 16 * (uintptr_t)rnd(0, 4096), w = 0x40000 + 16 * (uintptr_t)rnd(0, 4096);
+        const uintptr_t y = 0x30000 + 2 * (uintptr_t)rnd(0, 65536);
+        // now and then a workspace off its 256-byte alignment, which must be refused
+        const uintptr_t ws = 256 * (uintptr_t)rnd(1, 4096) + (rnd(0, 15) == 0 ? 16 : 0);
+        auto ptr = [](uintptr_t a) { return reinterpret_cast<void *>(a); };
+        const Call c = single_call(ptr(x), ptr(w), ptr(y), M, N, K, 0);
+        skinny_plan_t p{SKINNY_KIND_SPLIT_K, 64 * rnd(0, 10), 64, 1, 1, rnd(0, 70), rnd(0, 1), rnd(0, 1) * rnd(0, 4),
+                        rnd(0, 1) * rnd(0, 2), rnd(0, 1) * rnd(0, 2)};
+        const bool fields = split_fields_ok(p);
+        EXPECT(fields == (p.threads_per_block >= 64 && p.threads_per_block <= 512 && p.k_split >= 1 &&
+                          p.k_split <= 64 && p.nontemporal == 1 && p.grid_blocks == 0 && p.x_in_lds == 0 &&
+                          p.prefetch == 0),
+               "split fields decision");
+        if (!fields || validate(c) != SKINNY_OK || !split_call_ok(c))
+            continue;
+        const int rows_group = rnd(1, 4);
+        const SplitLayout l = split_layout(p.threads_per_block, rows_group, p.k_split, M, N);
+        const long long rows_t = (long long)(p.threads_per_block / 64) * rows_group;
+        EXPECT(l.tiles * rows_t >= N && (l.tiles - 1) * rows_t < N, "tiles do not cover N");
+        EXPECT(l.total == kSplitPartOffset + (size_t)p.k_split * M * N * 4, "layout size");
+        const size_t given = l.total + (size_t)rnd(-64, 64) * 4;
+        if (!split_layout_ok(l, p.k_split) || !split_workspace_ok(c, ptr(ws), given, l))
+            continue;
+        ++split_accepted;
+        EXPECT(given >= l.total && ws % 256 == 0, "accepted a small or misaligned workspace");
+        const uintptr_t lo = ws, hi = ws + l.total;
+        auto meets = [&](uintptr_t b, size_t n) { return n > 0 && b < hi && lo < b + n; };
+        EXPECT(!meets(x, span(M, K, K, 2)) && !meets(w, (size_t)N * K * 2) && !meets(y, (size_t)M * N * 2),
+               "accepted a workspace that meets x, W or y");
+        EXPECT(kSplitPartOffset >= (size_t)l.tiles * 4, "counters run into the partials");
+    }
+    // extreme sizes through the layout arithmetic (for the undefined-behaviour sanitizer)
+    for (int N : {1, 65536, 1 << 20, INT_MAX})
+        for (int S : {1, 16, 64})
+            for (int t : {64, 512}) {
+                const SplitLayout l = split_layout(t, 4, S, kMaxM, N);
+                EXPECT(l.tiles >= 1 && l.total > l.part_bytes, "extreme layout");
+                (void)split_layout_ok(l, S);
+            }
+
     std::printf("validate_fuzz: %ld accepted random calls, %ld disjoint pair views, %ld extreme calls "
-                "accepted, %ld cache keys, %d failures\n",
-                accepted, pairs_disjoint, extreme, nkeys, failures);
+                "accepted, %ld cache keys, %ld split-K workspaces accepted, %d failures\n",
+                accepted, pairs_disjoint, extreme, nkeys, split_accepted, failures);
     return failures == 0 ? 0 : 1;
 }
