@@ -230,9 +230,9 @@ const SplitVariant *find_split(const skinny_plan_t &p)
     return nullptr;
 }
 
-// Default split-K plan for K: 256 threads, one row per wave at 64 lanes per row,
-// the most slices in {4, 2, 8} order whose slice a compiled variant covers
-// (K = 4096: 4 slices of 1024); else 32 lanes per row.
+// Default split-K plan for K: 256 threads, one row per wave, 64 lanes per row
+// before 32, and the first slice count of 4, 2, 8 whose slice K / S a compiled
+// variant covers (K = 4096: 4 slices of 1024; K = 1536: 2 of 768 at 32 lanes).
 bool default_split(int K, int M, skinny_plan_t *out)
 {
     const int order[] = {4, 2, 8};
