@@ -615,24 +615,64 @@ def test_rejects_m9(skg):
                  torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda"))
 
 
-@pytest.mark.parametrize("kind", ["outlier", "scaled_up", "scaled_down", "sparse"])
+def _robust_x(kind, M, K, shape_id, tensor_id=0):
+    if kind == "outlier":
+        return synth.outlier_activations(M, K, seed=70, shape_id=shape_id, tensor_id=tensor_id)
+    if kind == "scaled_up":
+        return synth.scaled_activations(M, K, 8, seed=70, shape_id=shape_id, tensor_id=tensor_id)
+    if kind == "scaled_down":
+        return synth.scaled_activations(M, K, -8, seed=70, shape_id=shape_id, tensor_id=tensor_id)
+    return synth.sparse_activations(M, K, seed=70, shape_id=shape_id, tensor_id=tensor_id)
+
+
+ROBUST_KINDS = ["outlier", "scaled_up", "scaled_down", "sparse"]
+
+
+@pytest.mark.parametrize("kind", ROBUST_KINDS)
 def test_robustness_inputs(skg, kind):
     """Input classes beyond normal (vLLM PR #65306, section Validation): outlier,
-    scaled and sparse."""
-    for (N, K) in [(4096, 1024), (2048, 4096), (8192, 1536)]:
-        for M in (1, 4, 8):
-            if kind == "outlier":
-                x = synth.outlier_activations(M, K, seed=70, shape_id=N)
-            elif kind == "scaled_up":
-                x = synth.scaled_activations(M, K, 8, seed=70, shape_id=N)
-            elif kind == "scaled_down":
-                x = synth.scaled_activations(M, K, -8, seed=70, shape_id=N)
-            else:
-                x = synth.sparse_activations(M, K, seed=70, shape_id=N)
-            W = synth.weights(N, K, seed=70, shape_id=N)
-            y = skg.gemm(to_dev(x), to_dev(W))
+    scaled and sparse, on every single-GEMM shape of the decode projections
+    (whole outputs; the LM head at M = 1 and 4), through the table's plans."""
+    for (N, K) in CONFIG_SHAPES + [LM_HEAD]:
+        W = synth.weights(N, K, seed=70, shape_id=N)
+        Wd = to_dev(W)
+        for M in ((1, 4) if (N, K) == LM_HEAD else (1, 2, 4, 8)):
+            x = _robust_x(kind, M, K, N)
+            y = skg.gemm(to_dev(x), Wd)
             torch.cuda.synchronize()
             check(y, x, W, label=f"{kind} N={N} K={K} M={M}")
+
+
+@pytest.mark.parametrize("kind", ROBUST_KINDS)
+def test_robustness_inputs_other_entry_points(skg, kind):
+    """The same input classes through the paired, strided-pair, float32-output and
+    split-K entry points."""
+    N, K = 4096, 128
+    W0, W1 = synth.weights(N, K, seed=71, tensor_id=1), synth.weights(N, K, seed=71, tensor_id=2)
+    W0d, W1d = to_dev(W0), to_dev(W1)
+    for M in (1, 4, 8):
+        x = _robust_x(kind, M, K, 1, M)
+        y0, y1 = skg.gemm_pair(to_dev(x), W0d, W1d)
+        check(y0, x, W0, label=f"{kind} pair y0 M={M}")
+        check(y1, x, W1, label=f"{kind} pair y1 M={M}")
+        xm = _robust_x(kind, M, 2 * K, 2, M)
+        xmd = to_dev(xm)
+        z0, z1 = skg.gemm_pair_strided(xmd[:, :K], xmd[:, K:], W0d, W1d)
+        check(z0, np.ascontiguousarray(xm[:, :K]), W0, label=f"{kind} strided y0 M={M}")
+        check(z1, np.ascontiguousarray(xm[:, K:]), W1, label=f"{kind} strided y1 M={M}")
+    N, K = 288, 4096  # the router gate, float32 outputs
+    W = synth.weights(N, K, seed=72)
+    for M in (1, 4, 8):
+        x = _robust_x(kind, M, K, 3, M)
+        y = skg.gemm(to_dev(x), to_dev(W), out_dtype=torch.float32)
+        check_f32(y, x, W, label=f"{kind} f32out M={M}")
+    N, K = 2048, 4096  # split-K, default plan
+    W = synth.weights(N, K, seed=73)
+    Wd = to_dev(W)
+    for M in (1, 4, 8):
+        x = _robust_x(kind, M, K, 4, M)
+        y = skg.gemm_split_k(to_dev(x), Wd, skg.split_k_workspace(M, N, K))
+        check(y, x, W, label=f"{kind} split-K M={M}")
 
 
 def test_weight_beyond_4gib(skg):
