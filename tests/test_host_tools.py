@@ -418,3 +418,16 @@ def test_split_k_report(tmp_path):
     assert out[2] == "| (2048,4096) | 1 | 4.500 | 5.900 | 1.31 | (64, 2, 1, 4, 256) |"
     assert out[3] == "| (2048,4096) | 2 | 4.700 | 6.000 | 1.28 | (64, 2, 1, 2, 256) |"
     assert len(out) == 4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says so,
+    before touching any device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    res = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120, cwd=root)
+    assert res.returncode == 2, res.stderr
+    assert "one GPU" in res.stderr and res.stdout == ""
