@@ -7,7 +7,8 @@ tree; it is never installed into site-packages. Its translation units (the host
 side and the variant tables, which hold the kernel instances) are compiled in
 parallel into objects under _build/ and linked once. The read-stream probe used
 by the benchmark (include/skinny_stream_probe.h) is built beside it as
-libskinny_stream_probe.so.
+libskinny_stream_probe.so, and the torch operator (csrc/torch_op.cpp) as
+libskinny_torch_op.so, with the host compiler against torch's headers.
 """
 from __future__ import annotations
 
@@ -28,6 +29,11 @@ ARCH = "gfx950"
 SOURCES = ("skinny_gemm.hip", "variants_fixed_small.hip", "variants_fixed_k4096.hip",
            "variants_fixed_k8192.hip", "variants_other.hip", "split_k.hip")
 PROBE_LIB_PATH = os.path.join(HERE, "libskinny_stream_probe.so")
+# torch.ops.skinny.linear with its GPU kernel registered in C++ (a host-only
+# translation unit built with the host compiler against torch's headers; it
+# links the GEMM library above)
+TORCH_OP_PATH = os.path.join(HERE, "libskinny_torch_op.so")
+TORCH_OP_SOURCE = "torch_op.cpp"
 PROBE_SOURCES = ("stream_probe.hip",)
 
 # hipcc's host pass warns that it does not know the packed-fp32 feature; drop that noise
@@ -90,5 +96,47 @@ def build_library(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB_PATH
 
 
+def torch_op_commands(obj: str, out: str) -> list[list[str]]:
+    """g++ compile and link lines of the torch operator library."""
+    import torch
+    import torch.utils.cpp_extension as ce
+
+    abi = "1" if torch.compiled_with_cxx11_abi() else "0"
+    incs = [f"-I{d}" for d in ce.include_paths(device_type="cuda")] + ["-I", INCLUDE]
+    libs = ce.library_paths(device_type="cuda")
+    compile_cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", f"-D_GLIBCXX_USE_CXX11_ABI={abi}",
+                   "-DUSE_ROCM=1", "-D__HIP_PLATFORM_AMD__=1", *incs, "-c",
+                   os.path.join(CSRC, TORCH_OP_SOURCE), "-o", obj]
+    link_cmd = ["g++", "-shared", "-o", out, obj, f"-L{HERE}", "-lskinny_gemm_bf16",
+                *[f"-L{d}" for d in libs], "-lc10", "-lc10_hip", "-ltorch", "-ltorch_cpu",
+                "-ltorch_hip", "-lamdhip64", "-Wl,-rpath,$ORIGIN", *[f"-Wl,-rpath,{d}" for d in libs[:1]]]
+    return [compile_cmd, link_cmd]
+
+
+def build_torch_op(verbose: bool = False) -> str:
+    """Compile libskinny_torch_op.so (always recompiles); needs the GEMM library."""
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the GEMM library first")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    tag = f".{os.getpid()}"
+    obj = os.path.join(BUILD_DIR, "torch_op" + tag + ".o")
+    tmp = TORCH_OP_PATH + f".tmp{os.getpid()}"
+    try:
+        for cmd in torch_op_commands(obj, tmp):
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"building the torch op failed ({res.returncode}):\n{' '.join(cmd)}\n"
+                                   f"{res.stderr[-6000:]}")
+            if verbose and res.stderr.strip():
+                print(res.stderr, file=sys.stderr)
+        os.replace(tmp, TORCH_OP_PATH)
+    finally:
+        for f in (obj, tmp):
+            if os.path.exists(f):
+                os.remove(f)
+    return TORCH_OP_PATH
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_torch_op(verbose=True))

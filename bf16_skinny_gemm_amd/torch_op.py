@@ -8,7 +8,12 @@ linear path otherwise. Here:
 
 * ``torch.ops.skinny.linear(x, weight)`` is a custom operator (graph-capturable,
   with a fake implementation for tracing) that always runs the HIP kernel and
-  raises if the call does not qualify;
+  raises if the call does not qualify. Its GPU and CPU implementations are
+  registered in C++ (``libskinny_torch_op.so``, built from csrc/torch_op.cpp), so
+  an eager call goes from the dispatcher to the C ABI with no Python frame; when
+  that library has not been built, the same operator is registered from Python
+  below (it calls the same C entry point through ctypes, at a few µs more per
+  eager call);
 * :func:`skinny_linear` routes: qualifying calls go to the op, others to
   ``torch.nn.functional.linear`` only when ``fallback=True`` (the default for the
   module hook), else they raise;
@@ -24,10 +29,12 @@ refused launch raises.
 from __future__ import annotations
 
 import functools
+import os
 
 import torch
 
-from . import _on_device, _stream_handle, skinny_gemm_bf16
+from . import _on_device, _stream_handle, lib, skinny_gemm_bf16
+from .build import TORCH_OP_PATH
 
 _ARCH_OK: dict[int, bool] = {}
 
@@ -91,13 +98,22 @@ def _linear_fake(x: torch.Tensor, weight: torch.Tensor) -> torch.Tensor:
     return x.new_empty((*x.shape[:-1], weight.shape[0]))
 
 
-# The operator is registered through torch.library.Library rather than the
-# torch.library.custom_op decorator: the decorator's Python wrapping costs about
-# 10 us per eager call on its own, the plain registration about 3 us.
-_LIB = torch.library.Library("skinny", "DEF")
-_LIB.define("linear(Tensor x, Tensor weight) -> Tensor")
-_LIB.impl("linear", _linear_gpu, "CUDA")
-_LIB.impl("linear", _linear_other, "CPU")
+if os.path.exists(TORCH_OP_PATH):
+    # the C++ registration: schema and the CUDA / CPU kernels; the GEMM library it
+    # links is the one the ctypes binding loads (same file, one copy in the process)
+    lib()
+    torch.ops.load_library(TORCH_OP_PATH)
+    _LIB = torch.library.Library("skinny", "FRAGMENT")
+    CPP_OP = True
+else:
+    # The Python registration goes through torch.library.Library rather than the
+    # torch.library.custom_op decorator: the decorator's Python wrapping costs about
+    # 10 us per eager call on its own, the plain registration about 3 us.
+    _LIB = torch.library.Library("skinny", "DEF")
+    _LIB.define("linear(Tensor x, Tensor weight) -> Tensor")
+    _LIB.impl("linear", _linear_gpu, "CUDA")
+    _LIB.impl("linear", _linear_other, "CPU")
+    CPP_OP = False
 torch.library.register_fake("skinny::linear", _linear_fake, lib=_LIB)
 linear = torch.ops.skinny.linear
 
@@ -127,4 +143,4 @@ def install(module: torch.nn.Module, fallback: bool = True) -> int:
     return count
 
 
-__all__ = ["linear", "skinny_linear", "install", "qualifies"]
+__all__ = ["linear", "skinny_linear", "install", "qualifies", "CPP_OP"]

@@ -14,7 +14,9 @@ def op():
     from bf16_skinny_gemm_amd.build import LIB_PATH
     import os
 
-    if not os.path.exists(LIB_PATH):
+    from bf16_skinny_gemm_amd.build import TORCH_OP_PATH
+
+    if not os.path.exists(LIB_PATH) or not os.path.exists(TORCH_OP_PATH):
         import __graft_entry__
 
         __graft_entry__.build()
@@ -33,6 +35,21 @@ def test_cpu_tensors_route_to_fallback_or_raise(op):
         op.skinny_linear(x, w, fallback=False)
     with pytest.raises(ValueError):
         torch.ops.skinny.linear(x, w)
+
+
+def test_cpp_registration_when_built(op):
+    """With libskinny_torch_op.so built, the operator's kernels are the C++ ones:
+    the schema comes from it and a CPU call raises its ValueError."""
+    import os
+
+    from bf16_skinny_gemm_amd.build import TORCH_OP_PATH
+
+    assert op.CPP_OP == os.path.exists(TORCH_OP_PATH)
+    if not op.CPP_OP:
+        pytest.skip("the C++ operator library is not built")
+    assert str(torch.ops.skinny.linear.default._schema) == "skinny::linear(Tensor x, Tensor weight) -> Tensor"
+    with pytest.raises(ValueError, match="gfx950 GPU tensors only"):
+        torch.ops.skinny.linear(torch.zeros(1, 8, dtype=torch.bfloat16), torch.zeros(4, 8, dtype=torch.bfloat16))
 
 
 def test_fake_impl_shapes(op):
