@@ -154,3 +154,23 @@ def test_strided_weight_is_not_routed(op):
     assert torch.equal(op.skinny_linear(x, w), torch.nn.functional.linear(x, w))
     with pytest.raises(ValueError):
         torch.ops.skinny.linear(x, w)
+
+
+@pytest.mark.gpu
+def test_op_under_torch_compile(op):
+    """The op traces (its fake implementation gives the output metadata) and the
+    compiled function runs the same kernel: same bits as the eager call."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.manual_seed(2)
+    w = (torch.randn(4096, 1024, device="cuda") / 32).to(torch.bfloat16)
+    x = torch.randn(2, 3, 1024, device="cuda").to(torch.bfloat16)
+
+    def f(a, b):
+        return torch.ops.skinny.linear(a, b) * 2
+
+    compiled = torch.compile(f, backend="aot_eager", fullgraph=True)
+    y = compiled(x, w)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 3, 4096)
+    assert torch.equal(y.view(torch.int16), f(x, w).view(torch.int16))
