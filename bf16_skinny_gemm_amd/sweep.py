@@ -294,7 +294,10 @@ def measure(args):
     torch.cuda.set_device(dev)
     skg.skinny_gemm_init(0)
     done = done_keys(args.out)
-    cells = [(N, K, False) for (N, K) in SHAPES] + [(N, K, True) for (N, K) in PAIR_SHAPES]
+    if args.shapes:
+        cells = [tuple(int(v) for v in sh.split("x")) + (False,) for sh in args.shapes.split(",")]
+    else:
+        cells = [(N, K, False) for (N, K) in SHAPES] + [(N, K, True) for (N, K) in PAIR_SHAPES]
     if args.only:
         want = {tuple(int(v) for v in s.split("x")) for s in args.only.split(",")}
         cells = [c for c in cells if (c[0], c[1]) in want]
@@ -343,11 +346,16 @@ def measure(args):
                     plans = (refine_plans(skg, args.refine, N, K, M, pair, args.top, grids, args.twins)
                              if args.refine else candidate_plans(skg, K, M, kinds, grids))
                 current = None
-                if args.with_table and (N, K, M) in table:
-                    # the table's plan for the cell runs first and is always a finalist,
-                    # so a new plan replaces it only by beating it in the same rounds
-                    current = skg.Plan.from_dict(table[(N, K, M)])
-                    plans = [current] + [p for p in plans if plan_key(p) != plan_key(current)]
+                if args.with_table:
+                    # the table's plan for the cell (for a shape the table does not hold,
+                    # the library's default plan) runs first and is always a finalist, so
+                    # a new plan replaces it only by beating it in the same rounds
+                    if (N, K, M) in table:
+                        current = skg.Plan.from_dict(table[(N, K, M)])
+                    elif not pair:
+                        current = skg.skinny_gemm_get_plan(N, K, M)[0]
+                    if current is not None:
+                        plans = [current] + [p for p in plans if plan_key(p) != plan_key(current)]
                 staged = args.rounds > 1
 
                 def record(plan, us, lo, hi, stage):
@@ -356,6 +364,8 @@ def measure(args):
                            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)}
                     if staged:
                         rec["stage"] = stage
+                    if current is not None and plan_key(plan) == plan_key(current):
+                        rec["incumbent"] = True
                     fout.write(json.dumps(rec) + "\n")
 
                 warmed = False
@@ -471,15 +481,43 @@ def split_k_report(path) -> str:
     return "\n".join(rows)
 
 
+def incumbent_report(path) -> str:
+    """Per cell of a `--with-table` sweep: the incumbent plan (the table's, or the
+    library's default for a shape the table does not hold) against the fastest plan
+    timed, both from the same rounds (stage 2 when timed in rounds)."""
+    by = {}
+    with open(path) as f:
+        for line in f:
+            r = json.loads(line)
+            if "plan" in r:
+                by.setdefault((r["N"], r["K"], r["M"]), []).append(r)
+    rows = ["| (N, K) | M | incumbent µs | best µs | incumbent ÷ best | best plan |", "|---|---|---|---|---|---|"]
+    for (N, K, M) in sorted(by):
+        rs = by[(N, K, M)]
+        final = [r for r in rs if r.get("stage") == 2] or rs
+        inc = [r for r in final if r.get("incumbent")]
+        if not inc:
+            continue
+        b = min(final, key=lambda r: r["us"])
+        p = b["plan"]
+        desc = ", ".join(f"{k}={p[k]}" for k in PLAN_FIELDS)
+        rows.append(f"| ({N},{K}) | {M} | {inc[0]['us']:.3f} | {b['us']:.3f} | {inc[0]['us'] / b['us']:.3f} | {desc} |")
+    return "\n".join(rows)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--out", help="JSON-lines file to append measurements to")
     ap.add_argument("--emit-inc", metavar="JSONL[,JSONL...]",
                     help="write the plan table from sweep files (records pooled)")
     ap.add_argument("--inc-path", default=INC_PATH)
+    ap.add_argument("--incumbent-report", metavar="JSONL",
+                    help="print incumbent (table or default) plan vs fastest plan per cell of a --with-table sweep")
     ap.add_argument("--split-k-report", metavar="JSONL",
                     help="print table-plan vs split-K times per cell of a --kinds 5 --with-table sweep")
     ap.add_argument("--only", help="comma list of NxK shapes to sweep")
+    ap.add_argument("--shapes", help="comma list of NxK shapes to sweep instead of the decode "
+                    "projections (e.g. shapes outside the table, to rate the default plan)")
     ap.add_argument("--ms", default=",".join(str(m) for m in MS))
     ap.add_argument("--kinds", help="comma list of plan kinds to time (default: all)")
     ap.add_argument("--grids", default="persistent,tile",
@@ -506,6 +544,9 @@ def main():
     args = ap.parse_args()
     if args.split_k_report:
         print(split_k_report(args.split_k_report))
+        return 0
+    if args.incumbent_report:
+        print(incumbent_report(args.incumbent_report))
         return 0
     if args.emit_inc:
         print(emit_inc(args.emit_inc, args.inc_path))

@@ -453,3 +453,36 @@ def test_split_k_noalloc_refusals_need_no_device(skg):
     assert call(x + 8, W, y, 1, 1024, 4096, None, None) == E
     assert call(x, W, None, 1, 1024, 4096, None, None) == E
     assert call(None, None, None, 0, 1024, 4096, None, None) == skg.SKINNY_OK
+
+
+def test_default_plan_takes_nearest_tuned_neighbour(skg):
+    """A shape the table does not hold takes the tuned plan of the nearest N (by
+    ratio) with the same K and M, a tuned block count turned into the persistent
+    grid (0); a K the table never tuned takes looped-K, with 512 threads per block
+    once the staged x (M*K*2 bytes) reaches 32 KiB."""
+    import math
+
+    inc = os.path.join(ROOT, "bf16_skinny_gemm_amd", "csrc", "plans_gfx950.inc")
+    fields = ("kind", "threads_per_block", "lanes_per_row", "chunks", "rows_per_wave", "k_split",
+              "nontemporal", "grid_blocks", "x_in_lds", "prefetch")
+    table = {}
+    for n, k, m, f in re.findall(r"^\s*\{\s*(\d+),\s*(\d+),\s*(\d+),\s*\{([^}]*)\}\s*\},", open(inc).read(), re.M):
+        table[(int(n), int(k), int(m))] = dict(zip(fields, (int(v) for v in f.split(","))))
+    checked = 0
+    for N in (300, 1000, 3000, 6144, 9000, 14336, 30000, 100000):
+        for K in (1024, 1536, 4096, 8192):
+            for M in range(1, 9):
+                near = [(abs(math.log(n / N)), n) for (n, k, m) in table if k == K and m == M]
+                if not near or (N, K, M) in table:
+                    continue
+                want = dict(table[(min(near)[1], K, M)])
+                if 0 < want["grid_blocks"] < (1 << 20):
+                    want["grid_blocks"] = 0
+                p, tuned = skg.skinny_gemm_get_plan(N, K, M)
+                assert not tuned and p.as_dict() == want, (N, K, M, p, want)
+                checked += 1
+    assert checked > 100
+    for N, K, M, tpb in ((4096, 14336, 1, 256), (4096, 14336, 4, 512), (2048, 2048, 4, 256),
+                         (5120, 5120, 4, 512), (100, 1000, 2, 256)):
+        p, tuned = skg.skinny_gemm_get_plan(N, K, M)
+        assert not tuned and p.kind == skg.SKINNY_KIND_LOOP_K and p.threads_per_block == tpb, (N, K, M, p)
