@@ -363,13 +363,29 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 namespace {
 
 std::mutex g_scratch_mu;
-std::atomic<int> g_scratch_state[64];  // per device: 0 not set up, 1 ready, < 0 a status
+// per device: 0 nothing done, 2 address known (counters not yet cleared), 1 ready
+std::atomic<int> g_scratch_state[64];
 void *g_scratch_ptr[64];
 
-// Device address of the current GPU's copy of `scratch`, looked up once per device
-// with that device current. The first lookup also enqueues, on `stream`, a kernel
-// that zeroes the copy's counters (static storage starts at zero; the kernel makes
-// it explicit). Later calls find the counters at zero, as every call leaves them.
+// Looks up the current device's copy of `scratch` (caller holds g_scratch_mu).
+int scratch_lookup_locked(int dev)
+{
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return SKINNY_ERR_LAUNCH;  // nothing recorded: a later call tries again
+    }
+    g_scratch_ptr[dev] = p;
+    g_scratch_state[dev].store(2, std::memory_order_release);
+    return SKINNY_OK;
+}
+
+// Device address of the current GPU's copy of `scratch`, ready for a call on
+// `stream`. The address is looked up once per device, with that device current
+// (by skinny_gemm_init, or else here); the first call on the device also enqueues,
+// on its stream, a kernel that zeroes the copy's counters (static storage starts at
+// zero; the kernel makes it explicit, and a captured first call records it in its
+// graph). Later calls find the counters at zero, as every call leaves them.
 int scratch_ptr(hipStream_t stream, void **out)
 {
     int dev = -1;
@@ -379,27 +395,25 @@ int scratch_ptr(hipStream_t stream, void **out)
     }
     if (dev < 0 || dev >= 64)
         return SKINNY_ERR_UNSUPPORTED;
-    int state = g_scratch_state[dev].load(std::memory_order_acquire);
-    if (state == 0) {
+    if (g_scratch_state[dev].load(std::memory_order_acquire) != 1) {
         std::lock_guard<std::mutex> lk(g_scratch_mu);
-        state = g_scratch_state[dev].load(std::memory_order_relaxed);
+        int state = g_scratch_state[dev].load(std::memory_order_relaxed);
         if (state == 0) {
-            void *p = nullptr;
-            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
-                (void)hipGetLastError();
-                return SKINNY_ERR_LAUNCH;  // not cached: the next call tries again
-            }
-            unsigned *cnt = static_cast<unsigned *>(p);
+            const int st = scratch_lookup_locked(dev);
+            if (st != SKINNY_OK)
+                return st;
+            state = 2;
+        }
+        if (state == 2) {
+            unsigned *cnt = static_cast<unsigned *>(g_scratch_ptr[dev]);
             int n = (int)kSplitCountWords;
             void *args[] = {&cnt, &n};
             if (hipLaunchKernel(reinterpret_cast<const void *>(&skg::clear_words_kernel),
                                 dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, stream) != hipSuccess) {
                 (void)hipGetLastError();
-                return SKINNY_ERR_LAUNCH;
+                return SKINNY_ERR_LAUNCH;  // still 2: the next call clears them
             }
-            g_scratch_ptr[dev] = p;
-            state = 1;
-            g_scratch_state[dev].store(state, std::memory_order_release);
+            g_scratch_state[dev].store(1, std::memory_order_release);
         }
     }
     *out = g_scratch_ptr[dev];
@@ -407,6 +421,34 @@ int scratch_ptr(hipStream_t stream, void **out)
 }
 
 }  // namespace
+
+namespace skg_host {
+
+int split_k_scratch_setup(int dev)
+{
+    if (dev < 0 || dev >= 64)
+        return SKINNY_ERR_UNSUPPORTED;
+    if (g_scratch_state[dev].load(std::memory_order_acquire) != 0)
+        return SKINNY_OK;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_state[dev].load(std::memory_order_relaxed) != 0)
+        return SKINNY_OK;
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SKINNY_ERR_UNSUPPORTED;
+    }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return SKINNY_ERR_UNSUPPORTED;
+    }
+    const int st = scratch_lookup_locked(dev);
+    if (prev != dev && hipSetDevice(prev) != hipSuccess)
+        (void)hipGetLastError();
+    return st;
+}
+
+}  // namespace skg_host
 
 extern "C" {
 

@@ -174,4 +174,9 @@ inline bool split_workspace_ok(const Call &c, const void *ws, size_t bytes, cons
     return !overlaps(ws, l.total, c.x, xb) && !overlaps(ws, l.total, c.w0, wb) && !overlaps(ws, l.total, c.y0, yb);
 }
 
+// Looks up device `dev`'s copy of the allocation-free split-K entry point's static
+// workspace (split_k.hip), with that device made current for the lookup and the
+// caller's device restored; called by skinny_gemm_init. Returns a status code.
+int split_k_scratch_setup(int dev);
+
 }  // namespace skg_host

@@ -122,10 +122,13 @@ typedef struct skinny_plan {
                                   multiplied. Other kinds: always 0 */
 } skinny_plan_t;
 
-/* Checks that `device` is a gfx950 GPU and caches its properties. Optional:
- * every compute call performs the same check lazily on the current device.
- * Idempotent. Returns SKINNY_OK, SKINNY_ERR_INVALID_ARG (no such device) or
- * SKINNY_ERR_UNSUPPORTED (not gfx950). */
+/* Checks that `device` is a gfx950 GPU, caches its properties and looks up that
+ * device's copy of the static workspace of skinny_gemm_bf16_split_k_noalloc (with
+ * the device made current for the lookup, the caller's device restored after).
+ * Enqueues no work and allocates nothing. Optional: every compute call performs
+ * the same steps lazily on the current device. Idempotent. Returns SKINNY_OK,
+ * SKINNY_ERR_INVALID_ARG (no such device), SKINNY_ERR_UNSUPPORTED (not gfx950)
+ * or SKINNY_ERR_LAUNCH (the runtime refused the workspace lookup). */
 int skinny_gemm_init(int device);
 
 /* y = x . W^T with the plan the library's table holds for (N, K, M) on this
@@ -252,9 +255,10 @@ int skinny_gemm_bf16_split_k(const void *x, const void *W, void *y, int M, int N
  * workspace instead of a caller's. That workspace is one device array per GPU, in
  * the same layout (64 KiB of counters, then 4 MiB of partials), held from the
  * library's load until the process ends; a call whose S*M*N exceeds 2^20, or that
- * has more than 16384 row tiles, returns SKINNY_ERR_INVALID_ARG. The first call on
- * a GPU looks up that GPU's copy and enqueues one small kernel on `stream` that
- * zeroes its counters; no call allocates or frees memory. Every call on a GPU
+ * has more than 16384 row tiles, returns SKINNY_ERR_INVALID_ARG. skinny_gemm_init
+ * looks up each GPU's copy (else the first call on that GPU does); the first call
+ * on a GPU also enqueues one small kernel on `stream` that zeroes the copy's
+ * counters. No call allocates or frees memory. Every call on a GPU
  * shares that GPU's copy, so calls that may overlap on one GPU (other streams,
  * other host threads) race and must be serialised by the caller. */
 int skinny_gemm_bf16_split_k_noalloc(const void *x, const void *W, void *y, int M, int N, int K,

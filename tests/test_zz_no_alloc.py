@@ -126,6 +126,8 @@ sys.path.insert(0, sys.argv[1])
 import bf16_skinny_gemm_amd as skg
 dev = torch.device("cuda:0")
 torch.cuda.set_device(dev)
+if sys.argv[2] == "init":
+    skg.skinny_gemm_init(0)  # looks the workspace up; its counters are cleared by the first call
 g0 = torch.Generator(device=dev).manual_seed(23)
 N, K, M = 2048, 4096, 2
 W = (torch.randn(N, K, device=dev, generator=g0) / 64).to(torch.bfloat16)
@@ -151,16 +153,18 @@ print("ok")
 """
 
 
-def test_noalloc_first_call_inside_graph_capture(skg):
-    """A fresh process whose first no-alloc call is made under graph capture (its
-    set-up, the workspace lookup and the counter-clearing kernel, lands in the
-    graph): every replay gives the workspace entry point's bits."""
+@pytest.mark.parametrize("setup", ["init", "lazy"])
+def test_noalloc_first_call_inside_graph_capture(skg, setup):
+    """A fresh process whose first no-alloc call is made under graph capture, after
+    skinny_gemm_init (which looked the workspace up) or without it (the call looks it
+    up): the counter-clearing kernel of the first call lands in the graph, and every
+    replay gives the workspace entry point's bits."""
     import os
     import subprocess
     import sys
 
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    print("fresh process: first no-alloc call under capture, (2048,4096) M=2", flush=True)
-    res = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True, text=True,
-                         timeout=240)
+    print(f"fresh process ({setup}): first no-alloc call under capture, (2048,4096) M=2", flush=True)
+    res = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root, setup], capture_output=True,
+                         text=True, timeout=240)
     assert res.returncode == 0 and "ok" in res.stdout, res.stdout + res.stderr[-3000:]
