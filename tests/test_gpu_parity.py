@@ -917,3 +917,22 @@ def test_output_span_limits(skg):
             assert torch.all(buf[base + 3 * N:base + 4 * N] == -3.0)
     del buf
     torch.cuda.empty_cache()
+
+
+OFF_TABLE = [(14336, 4096), (4096, 14336), (6144, 4096), (5120, 5120), (2048, 2048), (1024, 8192),
+             (3000, 1536), (100000, 4096)]
+
+
+@pytest.mark.parametrize("N,K", OFF_TABLE, ids=lambda v: str(v))
+def test_default_plans_off_table_full(skg, N, K):
+    """Shapes the table does not hold run the default plan (the nearest tuned N's plan,
+    or looped-K for an untuned K) at full size, every M, whole outputs."""
+    W = synth.weights(N, K, seed=90, shape_id=N + K)
+    Wd = to_dev(W)
+    for M in range(1, 9):
+        plan, tuned = skg.skinny_gemm_get_plan(N, K, M)
+        assert not tuned
+        x = synth.activations(M, K, seed=90, shape_id=N + K, tensor_id=M)
+        y = skg.gemm(to_dev(x), Wd)
+        torch.cuda.synchronize()
+        check(y, x, W, label=f"default ({N},{K}) M={M} {plan}")
